@@ -1,0 +1,135 @@
+/*
+ * librelpos -- attention with a decomposed relative-position bias, for AMD
+ * Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and status codes.
+ *
+ * The operation (prhub summary page of vllm-project/vllm PR #55629, "DeepEncoder
+ * relative-position attention fused into a Triton kernel", section 关键源码片段,
+ * the RelPosAttention.forward branch):
+ *
+ *   tokens       i = qh*W + qw over an H x W grid, N = H*W (row-major flattening
+ *                of a [B, H, W, C] activation);
+ *   rel_h[i,kh]  = sum_c q[i,c] * rel_pos_h[qh - kh + H - 1, c]   (unscaled q)
+ *   rel_w[i,kw]  = sum_c q[i,c] * rel_pos_w[qw - kw + W - 1, c]
+ *   out[i,:]     = sum_j softmax_j( scale * q_i . k_j + rel_h[i, j/W] + rel_w[i, j%W] ) v[j,:]
+ *
+ * The page shows add_decomposed_rel_pos only as a call; the table index
+ * qh - kh + H - 1 (resp. qw - kw + W - 1) is the reading this library takes.
+ * The dense [B, heads, N, N] bias of the unfused path is never formed: the
+ * attention kernel streams K/V tiles with an online softmax (the page's
+ * implementation section, item 1) and adds the two bias terms per tile.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense, row-major, 16-byte aligned, and live in device
+ *     memory of the current HIP device (hipSetDevice).  The caller allocates and
+ *     owns every buffer; the library allocates nothing, keeps no state besides a
+ *     per-device cache of device properties, and never synchronises the host.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the null stream)
+ *     and completes asynchronously.  Calls are safe from several host threads.
+ *   - Checks run in this order, and the first failure is returned: sizes
+ *     (E_SHAPE), dtypes (E_DTYPE), scalars (E_VALUE); then, unless B*heads == 0
+ *     (an OK no-op), NULL pointers (E_NULL), alignment (E_ALIGN), overlap of an
+ *     output with any other operand (E_ALIAS), and finally that every pointer is
+ *     device memory of the current device whose allocation holds the whole
+ *     operand (E_DEVICE; a too-short allocation is E_SHAPE).
+ *   - On any validation failure nothing is launched and the status says why.
+ *     No call prints or throws.
+ */
+#ifndef RELPOS_H_
+#define RELPOS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RELPOS_ABI_VERSION 1
+
+typedef enum relpos_dtype {
+  RELPOS_BF16 = 0,
+  RELPOS_FP16 = 1,
+  RELPOS_FP32 = 2
+} relpos_dtype;
+
+typedef enum relpos_status {
+  RELPOS_OK = 0,
+  RELPOS_E_NULL = 1,    /* a required pointer is NULL */
+  RELPOS_E_SHAPE = 2,   /* a size is out of range (D != 64, H or W < 1, too large, ...) */
+  RELPOS_E_DTYPE = 3,   /* unsupported dtype or dtype combination */
+  RELPOS_E_ALIGN = 4,   /* a pointer is not 16-byte aligned */
+  RELPOS_E_DEVICE = 5,  /* a pointer is not device memory of the current device */
+  RELPOS_E_ALIAS = 6,   /* an output overlaps an input or the other output */
+  RELPOS_E_LAUNCH = 7,  /* the kernel launch failed (HIP error) */
+  RELPOS_E_HIP = 8,     /* another HIP runtime call failed */
+  RELPOS_E_VALUE = 9    /* a scalar argument is invalid (e.g. a non-finite scale) */
+} relpos_status;
+
+/*
+ * relpos_build: the per-query bias tables of the decomposed relative position.
+ *
+ * Defines (PR #55629 page, key source snippet, add_decomposed_rel_pos call):
+ *   rel_h[b,h,i,kh] = sum_c q[b,h,i,c] * rel_pos_h[i/W - kh + H - 1, c]
+ *   rel_w[b,h,i,kw] = sum_c q[b,h,i,c] * rel_pos_w[i%W - kw + W - 1, c]
+ * with bf16/fp16 products accumulated in fp32 and stored as fp32.
+ *
+ * Arguments (device pointers unless said otherwise):
+ *   q          [B, heads, H*W, D]   in_dtype  (the unscaled queries)
+ *   rel_pos_h  [2H-1, D]            in_dtype
+ *   rel_pos_w  [2W-1, D]            in_dtype
+ *   rel_h      [B, heads, H*W, H]   fp32, written
+ *   rel_w      [B, heads, H*W, W]   fp32, written
+ *   B, heads   >= 0, B*heads <= 65535 (B*heads == 0 is an OK no-op; pointers are then not read)
+ *   H, W       >= 1, H*W <= 2^24, H <= 4096, W <= 4096
+ *   D          must be 64
+ *   in_dtype   RELPOS_BF16 or RELPOS_FP16
+ *   stream     hipStream_t to enqueue on
+ * Errors: E_SHAPE, E_DTYPE, E_NULL, E_ALIGN, E_DEVICE, E_ALIAS (rel_h/rel_w
+ * overlapping each other or an input), E_LAUNCH.
+ */
+relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel_pos_w,
+                           float* rel_h, float* rel_w,
+                           int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                           relpos_dtype in_dtype, void* stream);
+
+/*
+ * relpos_attn_fwd: attention over all N = H*W keys with the decomposed bias.
+ *
+ * Defines (PR #55629 page, key source snippet, the SDPA fallback it replaces):
+ *   out[b,h,i,:] = sum_j P[i,j] v[b,h,j,:],
+ *   P[i,:] = softmax_j( scale * q[b,h,i,:] . k[b,h,j,:]
+ *                       + rel_h[b,h,i, j/W] + rel_w[b,h,i, j%W] ).
+ * Computed without the dense bias: K/V are streamed through LDS in tiles of
+ * the key grid, scores go through an exp2-based online softmax with fp32
+ * accumulators, and Q.K^T and P.V run on bf16/fp16 MFMA.
+ *
+ * Arguments (device pointers):
+ *   q, k, v    [B, heads, H*W, D]   in_dtype
+ *   rel_h      [B, heads, H*W, H]   fp32 (as written by relpos_build)
+ *   rel_w      [B, heads, H*W, W]   fp32
+ *   out        [B, heads, H*W, D]   out_dtype, written; must not overlap any input
+ *   B, heads   >= 0, B*heads <= 65535 (B*heads == 0 is an OK no-op)
+ *   H, W       >= 1, H*W <= 2^24, H <= 4096, W <= 4096
+ *   D          must be 64
+ *   scale      finite (else E_VALUE); multiplies q.k only (not the bias)
+ *   in_dtype   RELPOS_BF16 or RELPOS_FP16
+ *   out_dtype  RELPOS_FP32, or equal to in_dtype
+ *   stream     hipStream_t to enqueue on
+ * Errors: E_SHAPE, E_DTYPE, E_VALUE, E_NULL, E_ALIGN, E_DEVICE, E_ALIAS, E_LAUNCH.
+ */
+relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
+                              const float* rel_h, const float* rel_w, void* out,
+                              int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                              float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                              void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* relpos_status_string(relpos_status s);
+
+/* RELPOS_ABI_VERSION of the built library. */
+int relpos_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELPOS_H_ */

@@ -1,0 +1,141 @@
+"""ctypes binding of librelpos (include/relpos.h), same names as the C calls.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  Torch provides device memory (the output buffers are allocated here
+with torch, O(N*(D+H+W)) bytes) and the stream (torch's current stream).  There
+is no fallback: if the library is missing or a call fails, this raises.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librelpos.so")
+
+RELPOS_BF16, RELPOS_FP16, RELPOS_FP32 = 0, 1, 2
+_DT = {torch.bfloat16: RELPOS_BF16, torch.float16: RELPOS_FP16, torch.float32: RELPOS_FP32}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class RelposError(RuntimeError):
+    def __init__(self, call, status, message):
+        super().__init__(f"{call} failed: status {status} ({message})")
+        self.status = status
+
+
+def library_path():
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m relative_position_bias_relpos_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        lib.relpos_build.restype = i32
+        lib.relpos_build.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        lib.relpos_attn_fwd.restype = i32
+        lib.relpos_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+        lib.relpos_status_string.restype = ctypes.c_char_p
+        lib.relpos_status_string.argtypes = [i32]
+        lib.relpos_abi_version.restype = i32
+        lib.relpos_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def status_string(status):
+    return _load().relpos_status_string(int(status)).decode()
+
+
+def abi_version():
+    return _load().relpos_abi_version()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(call, status):
+    if status != 0:
+        raise RelposError(call, status, status_string(status))
+
+
+def _dims(q, H, W):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, heads, H*W, D]")
+    B, nh, N, D = q.shape
+    if N != H * W:
+        raise ValueError(f"q has {N} tokens but H*W = {H * W}")
+    return B, nh, D
+
+
+def _need(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def relpos_build(q, rel_pos_h, rel_pos_w, H, W, rel_h=None, rel_w=None):
+    """rel_h [B,heads,H*W,H], rel_w [B,heads,H*W,W] (fp32) from q and the tables."""
+    lib = _load()
+    B, nh, D = _dims(q, H, W)
+    _need(q, "q")
+    _need(rel_pos_h, "rel_pos_h", q.dtype)
+    _need(rel_pos_w, "rel_pos_w", q.dtype)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q must be bfloat16 or float16")
+    if rel_h is None:
+        rel_h = torch.empty((B, nh, H * W, H), dtype=torch.float32, device=q.device)
+    if rel_w is None:
+        rel_w = torch.empty((B, nh, H * W, W), dtype=torch.float32, device=q.device)
+    _need(rel_h, "rel_h", torch.float32)
+    _need(rel_w, "rel_w", torch.float32)
+    st = lib.relpos_build(_ptr(q), _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(rel_h), _ptr(rel_w),
+                          B, nh, H, W, D, _DT[q.dtype], _stream(q))
+    _check("relpos_build", st)
+    return rel_h, rel_w
+
+
+def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torch.float32):
+    """out [B,heads,H*W,D] = softmax(scale*q.k + rel_h[:, j/W] + rel_w[:, j%W]) @ v."""
+    lib = _load()
+    B, nh, D = _dims(q, H, W)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v must be bfloat16 or float16")
+    _need(rel_h, "rel_h", torch.float32)
+    _need(rel_w, "rel_w", torch.float32)
+    if tuple(rel_h.shape) != (B, nh, H * W, H) or tuple(rel_w.shape) != (B, nh, H * W, W):
+        raise ValueError("rel_h/rel_w must be [B, heads, H*W, H] and [B, heads, H*W, W]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need(out, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    st = lib.relpos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                             B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype], _stream(q))
+    _check("relpos_attn_fwd", st)
+    return out

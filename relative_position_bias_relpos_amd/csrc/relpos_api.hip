@@ -1,0 +1,200 @@
+// C ABI of librelpos: argument validation, operand checks and kernel launch.
+// Declared and documented in include/relpos.h.
+#include "../../include/relpos.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "relpos_kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxSide = 4096;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int64_t kMaxHeads = 65535;  // B*heads maps to grid.y
+constexpr int kMaxDevices = 64;
+
+struct Operand {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Operand& a, const Operand& b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+relpos_status check_dims(int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D, int64_t* BH) {
+  if (D != 64) return RELPOS_E_SHAPE;
+  if (B < 0 || heads < 0) return RELPOS_E_SHAPE;
+  if (H < 1 || W < 1 || H > kMaxSide || W > kMaxSide || H * W > kMaxTokens) return RELPOS_E_SHAPE;
+  if (heads != 0 && B > kMaxHeads / heads) return RELPOS_E_SHAPE;
+  *BH = B * heads;
+  return RELPOS_OK;
+}
+
+bool is_half(relpos_dtype t) { return t == RELPOS_BF16 || t == RELPOS_FP16; }
+
+relpos_status check_align(const Operand* ops, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (ops[i].p == nullptr) return RELPOS_E_NULL;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (reinterpret_cast<uintptr_t>(ops[i].p) & 15u) return RELPOS_E_ALIGN;
+  }
+  return RELPOS_OK;
+}
+
+// Every operand must be device memory of the current device, and its
+// allocation must hold the whole operand.  Failed queries leave no sticky
+// HIP error behind.
+relpos_status check_device(const Operand* ops, int n) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return RELPOS_E_HIP;
+  }
+  for (int i = 0; i < n; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ops[i].p) != hipSuccess) {
+      (void)hipGetLastError();
+      return RELPOS_E_DEVICE;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return RELPOS_E_DEVICE;
+    if (attr.device != dev) return RELPOS_E_DEVICE;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(ops[i].p)) != hipSuccess) {
+      (void)hipGetLastError();
+      return RELPOS_E_DEVICE;
+    }
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(ops[i].p);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
+    if (p0 + ops[i].bytes > b0 + size) return RELPOS_E_SHAPE;
+  }
+  return RELPOS_OK;
+}
+
+// Per-device cache of the LDS a workgroup may use.
+int device_lds_limit(int* out) {
+  static std::once_flag once[kMaxDevices];
+  static int limit[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  std::call_once(once[dev], [dev]() {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      v = 65536;
+    }
+    limit[dev] = v;
+  });
+  *out = limit[dev];
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int relpos_abi_version(void) { return RELPOS_ABI_VERSION; }
+
+const char* relpos_status_string(relpos_status s) {
+  switch (s) {
+    case RELPOS_OK: return "ok";
+    case RELPOS_E_NULL: return "a required pointer is NULL";
+    case RELPOS_E_SHAPE: return "a size is out of range or an allocation is too small";
+    case RELPOS_E_DTYPE: return "unsupported dtype or dtype combination";
+    case RELPOS_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case RELPOS_E_DEVICE: return "a pointer is not device memory of the current device";
+    case RELPOS_E_ALIAS: return "an output overlaps another operand";
+    case RELPOS_E_LAUNCH: return "kernel launch failed";
+    case RELPOS_E_HIP: return "a HIP runtime call failed";
+    case RELPOS_E_VALUE: return "a scalar argument is invalid";
+  }
+  return "unknown status";
+}
+
+relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel_pos_w,
+                           float* rel_h, float* rel_w,
+                           int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                           relpos_dtype in_dtype, void* stream) {
+  int64_t BH = 0;
+  relpos_status st = check_dims(B, heads, H, W, D, &BH);
+  if (st != RELPOS_OK) return st;
+  if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
+  if (BH == 0) return RELPOS_OK;
+
+  const size_t N = static_cast<size_t>(H * W);
+  const Operand ops[5] = {
+      {q, BH * N * 64 * 2},
+      {rel_pos_h, static_cast<size_t>(2 * H - 1) * 64 * 2},
+      {rel_pos_w, static_cast<size_t>(2 * W - 1) * 64 * 2},
+      {rel_h, BH * N * H * 4},
+      {rel_w, BH * N * W * 4},
+  };
+  if ((st = check_align(ops, 5)) != RELPOS_OK) return st;
+  for (int o = 3; o < 5; ++o) {
+    for (int i = 0; i < 5; ++i) {
+      if (i != o && overlaps(ops[o], ops[i])) return RELPOS_E_ALIAS;
+    }
+  }
+  if ((st = check_device(ops, 5)) != RELPOS_OK) return st;
+
+  relpos::BuildArgs a{q, rel_pos_h, rel_pos_w, rel_h, rel_w,
+                      static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W),
+                      in_dtype == RELPOS_BF16};
+  if (relpos::launch_build(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  return RELPOS_OK;
+}
+
+relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
+                              const float* rel_h, const float* rel_w, void* out,
+                              int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                              float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                              void* stream) {
+  int64_t BH = 0;
+  relpos_status st = check_dims(B, heads, H, W, D, &BH);
+  if (st != RELPOS_OK) return st;
+  if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
+  if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
+  if (!std::isfinite(scale)) return RELPOS_E_VALUE;
+  if (BH == 0) return RELPOS_OK;
+
+  const size_t N = static_cast<size_t>(H * W);
+  const size_t in_bytes = BH * N * 64 * 2;
+  const size_t out_bytes = BH * N * 64 * (out_dtype == RELPOS_FP32 ? 4 : 2);
+  const Operand ops[6] = {
+      {q, in_bytes}, {k, in_bytes}, {v, in_bytes},
+      {rel_h, BH * N * H * 4}, {rel_w, BH * N * W * 4}, {out, out_bytes},
+  };
+  if ((st = check_align(ops, 6)) != RELPOS_OK) return st;
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
+  }
+  if ((st = check_device(ops, 6)) != RELPOS_OK) return st;
+
+  int lds_limit = 0;
+  if (device_lds_limit(&lds_limit) != 0) return RELPOS_E_HIP;
+  int nw = 0;
+  for (int cand : {4, 2, 1}) {
+    if (relpos::attn_lds_bytes(cand, static_cast<int>(H), static_cast<int>(W)) <= static_cast<size_t>(lds_limit)) {
+      nw = cand;
+      break;
+    }
+  }
+  if (nw == 0) return RELPOS_E_SHAPE;
+
+  relpos::AttnArgs a{q, k, v, rel_h, rel_w, out,
+                     static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
+                     in_dtype == RELPOS_BF16, out_dtype == RELPOS_FP32};
+  if (relpos::launch_attn_fwd(a, nw, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  return RELPOS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+"""Helpers shared by the GPU tests: run the HIP path, run the oracle, compare."""
+
+import numpy as np
+import torch
+
+from oracle import relpos_oracle as O
+from relative_position_bias_relpos_amd import binding as rp
+from relative_position_bias_relpos_amd import inputs
+
+# Parity bar for the attention output against the float64 oracle.
+MAX_ABS = 2e-3
+MEAN_ABS = 1e-4
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def to_dev(d):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def gpu_run(d, out_dtype=torch.float32):
+    """relpos_build then relpos_attn_fwd on torch's current stream; synchronised."""
+    g = to_dev(d)
+    rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
+    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"],
+                             out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, rel_h, rel_w
+
+
+def oracle_full(d):
+    return O.relpos_attention(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(d["rel_pos_h"]),
+                              f64(d["rel_pos_w"]), d["H"], d["W"], d["scale"])
+
+
+def sample_rows(N, n, seed, H, W):
+    """Random query rows plus grid/tile boundary rows (first, last, row ends)."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, N - 1, W - 1, min(W, N - 1), N - W, 31, 32, 63, 64, 127, 128, 255, 256}
+    rows = set(int(x) for x in rng.choice(N, size=min(n, N), replace=False))
+    rows |= {r for r in fixed if 0 <= r < N}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def oracle_sampled(d, out_gpu, rows_per_head, seed=0, heads=None):
+    """Per (b, h), oracle rows vs the GPU rows; returns (abs errors array, count)."""
+    q, k, v = d["q"], d["k"], d["v"]
+    th, tw = f64(d["rel_pos_h"]), f64(d["rel_pos_w"])
+    B, nh, N, _ = q.shape
+    errs = []
+    pairs = [(b, h) for b in range(B) for h in range(nh)]
+    if heads is not None:
+        pairs = pairs[:heads]
+    for b, h in pairs:
+        rows = sample_rows(N, rows_per_head, seed + 97 * b + h, d["H"], d["W"])
+        ref = O.relpos_attention_rows(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), th, tw,
+                                      d["H"], d["W"], d["scale"], rows)
+        got = f64(out_gpu[b, h, rows])
+        errs.append(np.abs(got - ref).ravel())
+    return np.concatenate(errs)
+
+
+def rel_bound(q, table_rows_abs):
+    """Forward-error bound of an fp32-accumulated 64-term dot product of exact products."""
+    u = 2.0 ** -24
+    n = 64
+    gamma = n * u / (1 - n * u)
+    return gamma * table_rows_abs
+
+
+def build_bound(d, b, h):
+    """Elementwise bound gamma_64 * sum_c |q_c||T_c| for rel_h, rel_w of one head."""
+    qa = np.abs(f64(d["q"][b, h]))
+    bh, bw = O.rel_tables(qa, np.abs(f64(d["rel_pos_h"])), np.abs(f64(d["rel_pos_w"])), d["H"], d["W"])
+    return rel_bound(qa, bh), rel_bound(qa, bw)
+
+
+def make(name, seed=0, **kw):
+    return inputs.make(inputs.workload(name, **kw), seed=seed)

@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/relpos.h declares, and rejects bad arguments before touching the device.
+
+The validation order documented in the header (sizes, dtypes, scalars, then
+NULL, alignment and overlap) means these calls return before any HIP call, so
+fake pointer values are safe: they are compared, never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relpos.h")
+LIB = os.path.join(ROOT, "relative_position_bias_relpos_amd", "librelpos.so")
+
+BF16, FP16, FP32 = 0, 1, 2
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_DEVICE, E_ALIAS, E_LAUNCH, E_HIP, E_VALUE = range(10)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:relpos_status|const char\*|int)\s+(relpos_\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("librelpos.so not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB)
+    i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.relpos_build.restype = i32
+    lib.relpos_build.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.relpos_attn_fwd.restype = i32
+    lib.relpos_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.relpos_status_string.restype = ctypes.c_char_p
+    lib.relpos_status_string.argtypes = [i32]
+    return lib
+
+
+def test_header_declares_the_calls():
+    names = set(_declared())
+    assert {"relpos_build", "relpos_attn_fwd", "relpos_status_string", "relpos_abi_version"} <= names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    want = int(re.search(r"#define RELPOS_ABI_VERSION (\d+)", text).group(1))
+    assert lib.relpos_abi_version() == want
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(10):
+        s = lib.relpos_status_string(code)
+        assert s and s != b"unknown status"
+        seen.add(s)
+    assert len(seen) == 10
+    assert lib.relpos_status_string(99) == b"unknown status"
+
+
+P = [0x10000 * (i + 1) for i in range(6)]  # distinct, aligned, never dereferenced
+
+
+def attn(lib, ptrs=None, B=1, nh=2, H=4, W=4, D=64, scale=0.125, ind=BF16, outd=FP32):
+    p = ptrs or P
+    return lib.relpos_attn_fwd(*p, B, nh, H, W, D, scale, ind, outd, None)
+
+
+def build(lib, ptrs=None, B=1, nh=2, H=4, W=4, D=64, ind=BF16):
+    p = ptrs or P[:5]
+    return lib.relpos_build(*p, B, nh, H, W, D, ind, None)
+
+
+def test_shape_errors(lib):
+    assert attn(lib, D=32) == E_SHAPE
+    assert build(lib, D=128) == E_SHAPE
+    assert attn(lib, H=0) == E_SHAPE
+    assert attn(lib, W=-1) == E_SHAPE
+    assert attn(lib, H=5000) == E_SHAPE
+    assert attn(lib, H=4096, W=4097) == E_SHAPE
+    assert attn(lib, B=-1) == E_SHAPE
+    assert attn(lib, B=70000, nh=1) == E_SHAPE
+    assert build(lib, B=300, nh=300) == E_SHAPE
+
+
+def test_dtype_errors(lib):
+    assert attn(lib, ind=FP32) == E_DTYPE
+    assert attn(lib, ind=7) == E_DTYPE
+    assert attn(lib, ind=BF16, outd=FP16) == E_DTYPE
+    assert attn(lib, ind=FP16, outd=BF16) == E_DTYPE
+    assert build(lib, ind=FP32) == E_DTYPE
+
+
+def test_scale_must_be_finite(lib):
+    assert attn(lib, scale=float("nan")) == E_VALUE
+    assert attn(lib, scale=float("inf")) == E_VALUE
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert attn(lib, ptrs=[None] * 6, B=0) == OK
+    assert attn(lib, ptrs=[None] * 6, nh=0) == OK
+    assert build(lib, ptrs=[None] * 5, B=0) == OK
+
+
+def test_null_pointers(lib):
+    for i in range(6):
+        p = list(P)
+        p[i] = None
+        assert attn(lib, ptrs=p) == E_NULL
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert build(lib, ptrs=p) == E_NULL
+
+
+def test_misaligned(lib):
+    for i in range(6):
+        p = list(P)
+        p[i] += 2
+        assert attn(lib, ptrs=p) == E_ALIGN
+
+
+def test_aliasing(lib):
+    p = list(P)
+    p[5] = p[0]  # out == q
+    assert attn(lib, ptrs=p) == E_ALIAS
+    p = list(P)
+    p[5] = p[3] + 16  # out inside rel_h
+    assert attn(lib, ptrs=p) == E_ALIAS
+    p = list(P[:5])
+    p[4] = p[3]  # rel_w == rel_h
+    assert build(lib, ptrs=p) == E_ALIAS
+    p = list(P[:5])
+    p[3] = p[0]  # rel_h over q
+    assert build(lib, ptrs=p) == E_ALIAS
