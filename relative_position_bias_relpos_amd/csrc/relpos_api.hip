@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
 
 #include "relpos_kernels.hpp"
@@ -98,6 +99,18 @@ int device_lds_limit(int* out) {
   return 0;
 }
 
+// Order in which attention configurations are tried (first that fits LDS).
+constexpr int kAttnPreference[] = {0, 3, 4, 1, 2};
+
+// Tuning knob: RELPOS_ATTN_CFG=<0..4> forces one configuration when it fits
+// (read on every call, so one process can compare configurations).
+int forced_attn_config() {
+  const char* e = std::getenv("RELPOS_ATTN_CFG");
+  if (!e || !*e) return -1;
+  const int c = std::atoi(e);
+  return (c >= 0 && c < relpos::attn_num_configs()) ? c : -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,19 +194,24 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
 
   int lds_limit = 0;
   if (device_lds_limit(&lds_limit) != 0) return RELPOS_E_HIP;
-  int nw = 0;
-  for (int cand : {4, 2, 1}) {
+  int cfg = -1;
+  const int forced = forced_attn_config();
+  if (forced >= 0 && relpos::attn_lds_bytes(forced, static_cast<int>(H), static_cast<int>(W)) <=
+                         static_cast<size_t>(lds_limit)) {
+    cfg = forced;
+  }
+  for (int cand : kAttnPreference) {
+    if (cfg >= 0) break;
     if (relpos::attn_lds_bytes(cand, static_cast<int>(H), static_cast<int>(W)) <= static_cast<size_t>(lds_limit)) {
-      nw = cand;
-      break;
+      cfg = cand;
     }
   }
-  if (nw == 0) return RELPOS_E_SHAPE;
+  if (cfg < 0) return RELPOS_E_SHAPE;
 
   relpos::AttnArgs a{q, k, v, rel_h, rel_w, out,
                      static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
                      in_dtype == RELPOS_BF16, out_dtype == RELPOS_FP32};
-  if (relpos::launch_attn_fwd(a, nw, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  if (relpos::launch_attn_fwd(a, cfg, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
   return RELPOS_OK;
 }
 

@@ -3,23 +3,36 @@
 // item 1: K/V streamed with an online softmax, the bias slices loaded per key
 // block, no dense [N, N] bias).
 //
-// Layout of the work
-//   * A workgroup owns BM = 32*NW consecutive queries of one (batch, head); each
-//     of its NW waves owns 32 of them.
+// Work layout
+//   * A workgroup owns BM = 32*QT*NW consecutive queries of one (batch, head);
+//     each of its NW waves owns 32*QT of them (QT query tiles of 32).
 //   * Keys are visited in 2-D tiles of the key grid: 4 grid rows x 16 grid
-//     columns = 64 keys.  Inside a tile, key o (0..63) is grid cell
-//     (kh0 + o/16, kw0 + o%16).  Cells outside the grid are masked.
-//   * Scores are computed transposed, S^T = K * Q^T, with 32x32x16 MFMA: a lane
-//     then holds one query (lane%32) and 32 of the tile's keys, so row max and
-//     row sum need a single cross-lane step (lane ^ 32).
-//   * For the lane's keys o = 32*st + 8*g + 4*(lane/32) + e the grid offsets are
-//     r = o/16 = 2*st + g/2 and c = o%16 = 8*(g%2) + 4*(lane/32) + e, so the
-//     bias needs 4 rel_h values and 8 rel_w values per tile, read as three
-//     16-byte LDS loads.
-//   * O^T = V^T * P^T, again 32x32x16 MFMA, with P in fp16.  V tiles are stored
-//     transposed in LDS (d-major) with the keys of each 16-key step permuted so
-//     that a lane's eight keys are one 16-byte read.  bf16 V is converted to
-//     fp16 while staging (exact for |v| < 65520).
+//     columns = 64 keys, in column bands (kw0 outer, kh0 inner).  Key o
+//     (0..63) of a tile is grid cell (kh0 + o/16, kw0 + o%16); cells outside
+//     the grid are masked with a -inf bias.
+//   * Scores are computed transposed, S^T = K * Q^T, on 32x32x16 MFMA: a lane
+//     holds one query (lane%32) and 32 of the tile's keys,
+//     o = 32*st + 8*g + 4*(lane/32) + e, i.e. grid offsets r = 2*st + g/2 and
+//     c = 8*(g%2) + 4*(lane/32) + e.  Its bias therefore needs 8 rel_w values
+//     per column band (kept in registers for the whole band) and 4 rel_h
+//     values per tile (prefetched from global memory one tile ahead).  LDS
+//     holds only the double-buffered K/V tiles.
+//   * O^T += V^T * P^T, again 32x32x16 MFMA, with P in fp16.  V tiles are kept
+//     row-major in LDS and read with the gfx950 transpose read
+//     (ds_read_b64_tr_b16), which hands each lane four consecutive keys of one
+//     V column.  bf16 V is converted to fp16 while staging (exact for
+//     |v| < 65520).
+//
+// Online softmax (exp2 domain, scores pre-multiplied by log2 e)
+//   * Each query row keeps a reference maximum m.  Per tile,
+//     p = exp2(s*scale*log2e + rel_w' + (rel_h' - m)); the fp16 values of p
+//     are summed (v_dot2) into l and fed to the P.V MFMA.
+//   * m is only moved when it must be: on the first tile (exact tile maximum),
+//     and when some p of a tile exceeds 2^15, detected from the per-lane sum of
+//     the rounded p.  Then the tile's true maximum is taken, O and l are
+//     rescaled by exp2(m_old - m_new), and the tile's p are recomputed.  Between
+//     such events no rescale of O is needed; p stays <= 2^15 (finite in fp16)
+//     and the row's first maximum keeps l >= 1.
 #include "relpos_device.hpp"
 #include "relpos_kernels.hpp"
 
@@ -31,220 +44,292 @@ constexpr int kD = 64;
 constexpr int kTileKeys = 64;
 constexpr int kTileRows = 4;
 constexpr int kTileCols = 16;
-constexpr int kKStride = kD + 8;          // halves per K row in LDS (144 B)
-constexpr int kVStride = kTileKeys + 8;   // halves per V^T row in LDS (144 B)
+constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
+constexpr int kTileHalves = kTileKeys * kKStride;
+constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
 
-// LDS slot of key o inside its tile for the V^T layout: within each 16-key
-// group, bit 2 of o selects the lane half and bit 3 the second 4-key run.
-__device__ __forceinline__ int v_slot(int o) {
-  return (o & ~15) | (((o >> 2) & 1) << 3) | (((o >> 3) & 1) << 2) | (o & 3);
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read.  Within each 16-lane group, lane i receives
+// element (i % 4) of the 4-element row addressed by lane 4*k + i/4, k = 0..3.
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
-template <bool BF16, bool OUT_F32, int NW>
+// Logical work index of this workgroup.  Workgroups are dispatched round-robin
+// over the 8 XCDs; this maps the blocks that land on one XCD to a contiguous
+// range of (head, query tile) work so that a head's K/V stays in one XCD's L2.
+__device__ __forceinline__ int xcd_work_index(int G) {
+  const int L = blockIdx.x;
+  const int xcd = L & 7;
+  const int per = G >> 3, rem = G & 7;
+  const int start = xcd * per + (xcd < rem ? xcd : rem);
+  return start + (L >> 3);
+}
+
+template <bool BF16, bool OUT_F32, int NW, int QT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int Hp, int Wp, float c2) {
-  constexpr int BM = 32 * NW;
+    int H, int W, int q_tiles, float c2) {
+  constexpr int BM = 32 * QT * NW;
   constexpr int NT = NW * 64;
   const int N = H * W;
-  const int WSTR = Wp + 4;
-  const int HSTR = Hp + 4;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);         // [2][64][kKStride]
-  uint16_t* Vt = Ks + 2 * kTileKeys * kKStride;              // [2][64][kVStride]
-  float* rws = reinterpret_cast<float*>(Vt + 2 * kD * kVStride);  // [BM][WSTR]
-  float* rhs = rws + BM * WSTR;                                    // [BM][HSTR]
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [2][64][kKStride]
+  uint16_t* Vs = Ks + 2 * kTileHalves;                // [2][64][kKStride]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
-  const int q0 = blockIdx.x * BM;
-  const size_t head = static_cast<size_t>(blockIdx.y) * N;
 
-  // ---- per-workgroup bias rows, in log2 units, padding = -inf -------------
-  for (int idx = tid; idx < BM * Wp; idx += NT) {
-    const int r = idx / Wp, c = idx - r * Wp;
-    const int qi = q0 + r;
-    float val = -__builtin_inff();
-    if (c < W) val = (qi < N) ? rel_w[(head + qi) * W + c] * kLog2e : 0.f;
-    rws[r * WSTR + c] = val;
-  }
-  for (int idx = tid; idx < BM * Hp; idx += NT) {
-    const int r = idx / Hp, c = idx - r * Hp;
-    const int qi = q0 + r;
-    float val = -__builtin_inff();
-    if (c < H) val = (qi < N) ? rel_h[(head + qi) * H + c] * kLog2e : 0.f;
-    rhs[r * HSTR + c] = val;
-  }
+  const int G = static_cast<int>(gridDim.x);
+  const int work = xcd_work_index(G);
+  const int bh = work / q_tiles;
+  const int q0 = (work - bh * q_tiles) * BM;
+  const size_t head = static_cast<size_t>(bh) * N;
 
-  // ---- this lane's query: Q^T operand fragments (4 k-steps of 16) ---------
-  const int qrow = wave * 32 + (lane & 31);
-  const int qi = q0 + qrow;
-  u32x4 qf[4];
+  // ---- this lane's queries: Q^T operand fragments (4 k-steps of 16) -------
+  int qrow[QT];
+  u32x4 qf[QT][4];
 #pragma unroll
-  for (int kd = 0; kd < 4; ++kd) {
-    qf[kd] = (qi < N) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
-                      : u32x4{0, 0, 0, 0};
+  for (int t = 0; t < QT; ++t) {
+    qrow[t] = (wave * QT + t) * 32 + (lane & 31);
+    const int qi = q0 + qrow[t];
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      qf[t][kd] = (qi < N) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
+                           : u32x4{0, 0, 0, 0};
+    }
   }
 
   const int nWt = (W + kTileCols - 1) / kTileCols;
   const int nHt = (H + kTileRows - 1) / kTileRows;
   const int T = nWt * nHt;
 
-  // ---- K/V tile staging: global -> registers -> LDS ------------------------
-  constexpr int KCH = (kTileKeys * kD / 8) / NT;   // 16-byte K chunks per thread
-  constexpr int VPT = (kTileKeys / 2) * (kD / 8) / NT;  // (key pair, d chunk) tasks per thread
-  static_assert(KCH >= 1 && VPT >= 1, "workgroup too large for one tile");
-  u32x4 kreg[KCH];
-  u32x4 vreg[VPT][2];
+  // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
+  constexpr int CH = (kTileKeys * kD / 8) / NT;  // 16-byte chunks of K (and of V) per thread
+  static_assert(CH >= 1, "workgroup too large for one tile");
+  int ch_r[CH], ch_c[CH], ch_off[CH], ch_lds[CH];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    const int cid = tid + s * NT;
+    const int o = cid >> 3, dc = cid & 7;
+    ch_r[s] = o >> 4;
+    ch_c[s] = o & 15;
+    ch_off[s] = (o >> 4) * W + (o & 15);
+    ch_lds[s] = o * kKStride + 8 * dc;
+  }
+  const int dcol = 8 * (tid & 7);
+  u32x4 kreg[CH], vreg[CH];
 
-  auto key_of = [&](int t, int o, bool& ok) -> int {
-    const int kh = (t / nWt) * kTileRows + (o >> 4);
-    const int kw = (t % nWt) * kTileCols + (o & 15);
-    ok = (kh < H) && (kw < W);
-    return kh * W + kw;
-  };
   auto load_tile = [&](int t) {
+    const int tb = t / nHt;
+    const int kw0 = tb * kTileCols, kh0 = (t - tb * nHt) * kTileRows;
+    const size_t base = head + static_cast<size_t>(kh0) * W + kw0;
 #pragma unroll
-    for (int s = 0; s < KCH; ++s) {
-      const int cid = tid + s * NT;
-      const int o = cid >> 3, ch = cid & 7;
-      bool ok;
-      const int j = key_of(t, o, ok);
-      kreg[s] = ok ? *reinterpret_cast<const u32x4*>(k + (head + j) * kD + 8 * ch) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-      const int task = tid + s * NT;
-      const int p = task >> 3, dc = task & 7;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bool ok;
-        const int j = key_of(t, 2 * p + u, ok);
-        vreg[s][u] = ok ? *reinterpret_cast<const u32x4*>(v + (head + j) * kD + 8 * dc) : u32x4{0, 0, 0, 0};
-      }
+    for (int s = 0; s < CH; ++s) {
+      const bool ok = (kh0 + ch_r[s] < H) && (kw0 + ch_c[s] < W);
+      const size_t e = (base + ch_off[s]) * kD + dcol;
+      kreg[s] = ok ? *reinterpret_cast<const u32x4*>(k + e) : u32x4{0, 0, 0, 0};
+      vreg[s] = ok ? *reinterpret_cast<const u32x4*>(v + e) : u32x4{0, 0, 0, 0};
     }
   };
   auto store_tile = [&](int buf) {
-    uint16_t* kb = Ks + buf * kTileKeys * kKStride;
-    uint16_t* vb = Vt + buf * kD * kVStride;
+    uint16_t* kb = Ks + buf * kTileHalves;
+    uint16_t* vb = Vs + buf * kTileHalves;
 #pragma unroll
-    for (int s = 0; s < KCH; ++s) {
-      const int cid = tid + s * NT;
-      const int o = cid >> 3, ch = cid & 7;
-      *reinterpret_cast<u32x4*>(kb + o * kKStride + 8 * ch) = kreg[s];
-    }
+    for (int s = 0; s < CH; ++s) {
+      *reinterpret_cast<u32x4*>(kb + ch_lds[s]) = kreg[s];
+      u32x4 x = vreg[s];
+      if constexpr (BF16) {
 #pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-      const int task = tid + s * NT;
-      const int p = task >> 3, dc = task & 7;
-      const int slot = v_slot(2 * p);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = vreg[s][0][w], b = vreg[s][1][w];
-        uint32_t lo, hi;  // (key 2p, key 2p+1) pairs for d = 8dc+2w and 8dc+2w+1
-        if constexpr (BF16) {
-          lo = pack_f16(bf16_lo(a), bf16_lo(b));
-          hi = pack_f16(bf16_hi(a), bf16_hi(b));
-        } else {
-          lo = (a & 0xffffu) | (b << 16);
-          hi = (a >> 16) | (b & 0xffff0000u);
-        }
-        const int d = 8 * dc + 2 * w;
-        *reinterpret_cast<uint32_t*>(vb + d * kVStride + slot) = lo;
-        *reinterpret_cast<uint32_t*>(vb + (d + 1) * kVStride + slot) = hi;
+        for (int w = 0; w < 4; ++w) x[w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
       }
+      *reinterpret_cast<u32x4*>(vb + ch_lds[s]) = x;
     }
   };
 
+  // rel_w' (x log2 e) for the lane's 8 key columns of a band; -inf outside the grid.
+  const float* rw_row[QT];
+  const float* rh_row[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int qi = q0 + qrow[t];
+    const size_t qq = head + static_cast<size_t>(qi < N ? qi : 0);
+    rw_row[t] = rel_w + qq * W;
+    rh_row[t] = rel_h + qq * H;
+  }
+  float rw[QT][8];
+  auto load_band = [&](int kw0) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        rw[qt][i] = (c < W) ? rw_row[qt][c] * kLog2e : -__builtin_inff();
+      }
+  };
+  float rhn[QT][4];  // rel_h' of the next tile's 4 grid rows
+  auto load_rh = [&](int t) {
+    const int kh0 = (t - (t / nHt) * nHt) * kTileRows;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rhn[qt][r] = (kh0 + r < H) ? rh_row[qt][kh0 + r] * kLog2e : -__builtin_inff();
+  };
+
   load_tile(0);
+  load_rh(0);
   store_tile(0);
 
-  f32x16 acc[2];
+  f32x16 acc[QT][2];
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) acc[dt] = f32x16{};
-  float m = -__builtin_inff();
-  float l = 0.f;
+  for (int t = 0; t < QT; ++t) {
+    acc[t][0] = f32x16{};
+    acc[t][1] = f32x16{};
+  }
+  float m[QT], l[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m[t] = 0.f;
+    l[t] = 0.f;
+  }
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  // transpose-read lane addressing for the V^T operand (see header comment)
+  const int grp = lane >> 4, jl = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (jl >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
 
   for (int t = 0; t < T; ++t) {
     __syncthreads();
     const int buf = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
-    const uint16_t* kb = Ks + buf * kTileKeys * kKStride;
-    const uint16_t* vb = Vt + buf * kD * kVStride;
-    const int kh0 = (t / nWt) * kTileRows;
-    const int kw0 = (t % nWt) * kTileCols;
+    const int tb = t / nHt;
+    if (t == tb * nHt) load_band(tb * kTileCols);
+    float rh[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rh[qt][r] = rhn[qt][r];
+    if (t + 1 < T) {
+      load_tile(t + 1);
+      load_rh(t + 1);
+    }
+    const uint16_t* kb = Ks + buf * kTileHalves;
+    const uint16_t* vb = Vs + buf * kTileHalves;
 
-    // S^T = K Q^T for the tile's 64 keys (two 32-key halves).
-    f32x16 s[2];
+    // K^T fragments are shared by this wave's query tiles.
+    u32x4 kf[2][4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = f32x16{};
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int kd = 0; kd < 4; ++kd) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
-        s[st] = mfma32<BF16>(kf, qf[kd], s[st]);
+      for (int kd = 0; kd < 4; ++kd)
+        kf[st][kd] = *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
+
+    u32x4 pf[QT][4];
+    float tsum[QT];
+    f32x16 s[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s[qt][st] = f32x16{};
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) s[qt][st] = mfma32<BF16>(kf[st][kd], qf[qt][kd], s[qt][st]);
       }
     }
 
-    // bias, in log2 units: t = s*scale*log2e + rel_h' + rel_w'
-    const f32x4 rw0 = *reinterpret_cast<const f32x4*>(rws + qrow * WSTR + kw0 + 4 * half);
-    const f32x4 rw1 = *reinterpret_cast<const f32x4*>(rws + qrow * WSTR + kw0 + 8 + 4 * half);
-    const f32x4 rh = *reinterpret_cast<const f32x4*>(rhs + qrow * HSTR + kh0);
-    float mloc = -__builtin_inff();
+    bool grow = (t == 0);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int qt = 0; qt < QT; ++qt) {
+      float ts = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float rhv = rh[2 * st + (g >> 1)];
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float rwv = (g & 1) ? rw1[e] : rw0[e];
-          const float x = __builtin_fmaf(s[st][4 * g + e], c2, rhv + rwv);
-          s[st][4 * g + e] = x;
-          mloc = __builtin_fmaxf(mloc, x);
+        for (int g = 0; g < 4; ++g) {
+          const float rhm = rh[qt][2 * st + (g >> 1)] - m[qt];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float b = rw[qt][4 * (g & 1) + e] + rhm;
+            s[qt][st][4 * g + e] = __builtin_fmaf(s[qt][st][4 * g + e], c2, b);
+          }
+        }
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            w4[i] = pack_f16(exp2_fast(s[qt][st][8 * gg + 2 * i]), exp2_fast(s[qt][st][8 * gg + 2 * i + 1]));
+            ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
+          }
+          pf[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
       }
+      tsum[qt] = ts;
+      grow = grow || !(ts <= kGrowLimit);
     }
-    mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = __builtin_fmaxf(m, mloc);
-    const float alpha = exp2_fast(m - m_new);
-    m = m_new;
 
-    // p = exp2(t - m), rounded to fp16; the row sum uses the rounded values.
-    u32x4 pf[4];
-    float lt = 0.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // Move the reference maximum: exact tile maximum per query, then
+      // rescale O and l and recompute this tile's p against the new m.
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+      for (int qt = 0; qt < QT; ++qt) {
+        float mx = -__builtin_inff();
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        uint32_t w4[4];
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = exp2_fast(s[st][8 * gg + 2 * i] - m_new);
-          const float p1 = exp2_fast(s[st][8 * gg + 2 * i + 1] - m_new);
-          w4[i] = pack_f16(p0, p1);
-          lt = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, lt, false);
+          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qt][st][r]);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        float inc;
+        if (t == 0) {
+          inc = mx;  // O and l are still zero: only set m
+        } else {
+          inc = __builtin_fmaxf(mx, 0.f);
+          const float alpha = exp2_fast(-inc);
+          l[qt] *= alpha;
+          acc[qt][0] *= alpha;
+          acc[qt][1] *= alpha;
         }
-        pf[2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        m[qt] += inc;
+        float ts = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              w4[i] = pack_f16(exp2_fast(s[qt][st][8 * gg + 2 * i] - inc),
+                               exp2_fast(s[qt][st][8 * gg + 2 * i + 1] - inc));
+              ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
+            }
+            pf[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+          }
+        }
+        tsum[qt] = ts;
       }
     }
-    l = l * alpha + lt;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) acc[dt] *= alpha;
 
     // O^T += V^T P^T: four 16-key steps, two 32-row d tiles.
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) l[qt] += tsum[qt];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vb + (32 * dt + (lane & 31)) * kVStride + 16 * ks + 8 * half);
-        acc[dt] = mfma32<false>(vf, pf[ks], acc[dt]);
+        const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
+        const u32x2 lo = ds_read_tr16(vp);
+        const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf, pf[qt][ks], acc[qt][dt]);
       }
     }
 
@@ -252,16 +337,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
-  l += __shfl_xor(l, 32);
-  if (qi < N) {
-    const float inv = 1.0f / l;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float lt = l[qt] + __shfl_xor(l[qt], 32);
+    const int qi = q0 + qrow[qt];
+    if (qi >= N) continue;
+    const float inv = 1.0f / lt;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * half;
-        const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
-                          acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
+        const f32x4 o4 = {acc[qt][dt][4 * g] * inv, acc[qt][dt][4 * g + 1] * inv,
+                          acc[qt][dt][4 * g + 2] * inv, acc[qt][dt][4 * g + 3] * inv};
         if constexpr (OUT_F32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
         } else {
@@ -274,45 +362,51 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32, int NW>
-hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
-  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW>;
+template <bool BF16, bool OUT_F32, int NW, int QT>
+hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
+  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, QT>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
-  constexpr int BM = 32 * NW;
-  dim3 grid(static_cast<unsigned>((a.H * a.W + BM - 1) / BM), static_cast<unsigned>(a.BH));
+  constexpr int BM = 32 * NW * QT;
+  const int q_tiles = (a.H * a.W + BM - 1) / BM;
+  dim3 grid(static_cast<unsigned>(q_tiles * a.BH));
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, round_up(a.H, kTileRows), round_up(a.W, kTileCols),
-                     a.scale * kLog2e);
+                     a.H, a.W, q_tiles, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <bool BF16, bool OUT_F32>
-hipError_t launch_dt(const AttnArgs& a, int nw, size_t lds, hipStream_t stream) {
-  switch (nw) {
-    case 4: return launch_nw<BF16, OUT_F32, 4>(a, lds, stream);
-    case 2: return launch_nw<BF16, OUT_F32, 2>(a, lds, stream);
-    default: return launch_nw<BF16, OUT_F32, 1>(a, lds, stream);
+hipError_t launch_dt(const AttnArgs& a, int cfg, size_t lds, hipStream_t stream) {
+  switch (cfg) {
+    case 0: return launch_cfg<BF16, OUT_F32, 4, 1>(a, lds, stream);
+    case 1: return launch_cfg<BF16, OUT_F32, 2, 1>(a, lds, stream);
+    case 2: return launch_cfg<BF16, OUT_F32, 1, 1>(a, lds, stream);
+    case 3: return launch_cfg<BF16, OUT_F32, 4, 2>(a, lds, stream);
+    default: return launch_cfg<BF16, OUT_F32, 2, 2>(a, lds, stream);
   }
 }
+
 
 }  // namespace
 
-size_t attn_lds_bytes(int nw, int H, int W) {
-  const size_t kv = 2 * (size_t)kTileKeys * kKStride * 2 + 2 * (size_t)kD * kVStride * 2;
-  const size_t rel = (size_t)32 * nw * ((round_up(W, kTileCols) + 4) + (round_up(H, kTileRows) + 4)) * 4;
-  return kv + rel;
+int attn_num_configs() { return 5; }
+
+size_t attn_lds_bytes(int cfg, int H, int W) {
+  (void)cfg;
+  (void)H;
+  (void)W;
+  return 2 * 2 * static_cast<size_t>(kTileHalves) * 2;  // K and V, double-buffered
 }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, int nw, hipStream_t stream) {
-  const size_t lds = attn_lds_bytes(nw, a.H, a.W);
+hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
+  const size_t lds = attn_lds_bytes(cfg, a.H, a.W);
   if (a.bf16) {
-    return a.out_f32 ? launch_dt<true, true>(a, nw, lds, stream) : launch_dt<true, false>(a, nw, lds, stream);
+    return a.out_f32 ? launch_dt<true, true>(a, cfg, lds, stream) : launch_dt<true, false>(a, cfg, lds, stream);
   }
-  return a.out_f32 ? launch_dt<false, true>(a, nw, lds, stream) : launch_dt<false, false>(a, nw, lds, stream);
+  return a.out_f32 ? launch_dt<false, true>(a, cfg, lds, stream) : launch_dt<false, false>(a, cfg, lds, stream);
 }
 
 }  // namespace relpos

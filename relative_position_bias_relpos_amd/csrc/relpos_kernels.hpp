@@ -34,8 +34,11 @@ struct AttnArgs {
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
-// LDS bytes the attention kernel needs with `nw` waves per workgroup.
-size_t attn_lds_bytes(int nw, int H, int W);
-hipError_t launch_attn_fwd(const AttnArgs& a, int nw, hipStream_t stream);
+// Attention launch configurations (waves per workgroup x 32-query tiles per
+// wave): 0: 4x1, 1: 2x1, 2: 1x1, 3: 4x2, 4: 2x2.
+int attn_num_configs();
+// LDS bytes the attention kernel needs in configuration `cfg`.
+size_t attn_lds_bytes(int cfg, int H, int W);
+hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
 
 }  // namespace relpos

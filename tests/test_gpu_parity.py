@@ -149,3 +149,16 @@ def test_no_allocation_during_calls():
     assert torch.cuda.max_memory_allocated() == before
     # A dense bf16 bias for this workload would be 384 MiB; nothing of that order appears.
     assert abs(free_before - free_after) < 2 * 1024 * 1024
+
+
+# ---- every launch configuration ------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("rect", dict(B=1, heads=2, H=21, W=35)),
+                                     ("batched_fp16", dict(B=1, heads=2, H=20, W=24))])
+def test_each_launch_config(cfg, name, kw, monkeypatch):
+    monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
+    d = G.make(name, **kw)
+    out, _, _ = G.gpu_run(d)
+    ref, _, _ = G.oracle_full(d)
+    _check(f"cfg{cfg} {name}", np.abs(G.f64(out) - ref))
