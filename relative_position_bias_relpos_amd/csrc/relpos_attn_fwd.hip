@@ -58,6 +58,22 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Raw buffer loads: an offset at or past the resource's byte size returns
+// zeros in hardware, which masks grid cells outside the tile without branches.
+constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw-buffer descriptor word 3
+constexpr int kOob = 0x7ffffff0;             // any offset past every resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                          static_cast<int>(kBufFlags));
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Logical work index of this workgroup.  Workgroups are dispatched round-robin
 // over the 8 XCDs; this maps the blocks that land on one XCD to a contiguous
 // range of (head, query tile) work so that a head's K/V stays in one XCD's L2.
@@ -127,17 +143,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
   const int dcol = 8 * (tid & 7);
   u32x4 kreg[CH], vreg[CH];
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head * kD, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head * kD, head_bytes);
 
-  auto load_tile = [&](int t) {
-    const int tb = t / nHt;
-    const int kw0 = tb * kTileCols, kh0 = (t - tb * nHt) * kTileRows;
-    const size_t base = head + static_cast<size_t>(kh0) * W + kw0;
+  // Tile t covers grid rows [kh0, kh0+4) and columns [kw0, kw0+16).
+  auto load_tile = [&](int kh0, int kw0) {
+    const int base = kh0 * W + kw0;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
       const bool ok = (kh0 + ch_r[s] < H) && (kw0 + ch_c[s] < W);
-      const size_t e = (base + ch_off[s]) * kD + dcol;
-      kreg[s] = ok ? *reinterpret_cast<const u32x4*>(k + e) : u32x4{0, 0, 0, 0};
-      vreg[s] = ok ? *reinterpret_cast<const u32x4*>(v + e) : u32x4{0, 0, 0, 0};
+      const int off = ok ? ((base + ch_off[s]) * kD + dcol) * 2 : kOob;
+      kreg[s] = buf_load16(krs, off);
+      vreg[s] = buf_load16(vrs, off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -155,15 +173,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
   };
 
-  // rel_w' (x log2 e) for the lane's 8 key columns of a band; -inf outside the grid.
-  const float* rw_row[QT];
-  const float* rh_row[QT];
+  // rel_w' (x log2 e) for the lane's 8 key columns of a band and rel_h' for
+  // the 4 grid rows of a tile; -inf outside the grid.
+  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
+  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
+  int rw_off[QT], rh_off[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int qi = q0 + qrow[t];
-    const size_t qq = head + static_cast<size_t>(qi < N ? qi : 0);
-    rw_row[t] = rel_w + qq * W;
-    rh_row[t] = rel_h + qq * H;
+    rw_off[t] = (qi < N ? qi : 0) * W * 4;
+    rh_off[t] = (qi < N ? qi : 0) * H * 4;
   }
   float rw[QT][8];
   auto load_band = [&](int kw0) {
@@ -172,20 +191,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        rw[qt][i] = (c < W) ? rw_row[qt][c] * kLog2e : -__builtin_inff();
+        const float x = buf_loadf(rwrs, c < W ? rw_off[qt] + 4 * c : kOob);
+        rw[qt][i] = (c < W) ? x * kLog2e : -__builtin_inff();
       }
   };
   float rhn[QT][4];  // rel_h' of the next tile's 4 grid rows
-  auto load_rh = [&](int t) {
-    const int kh0 = (t - (t / nHt) * nHt) * kTileRows;
+  auto load_rh = [&](int kh0) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rhn[qt][r] = (kh0 + r < H) ? rh_row[qt][kh0 + r] * kLog2e : -__builtin_inff();
+      for (int r = 0; r < 4; ++r) {
+        const float x = buf_loadf(rhrs, kh0 + r < H ? rh_off[qt] + 4 * (kh0 + r) : kOob);
+        rhn[qt][r] = (kh0 + r < H) ? x * kLog2e : -__builtin_inff();
+      }
   };
 
-  load_tile(0);
+  load_tile(0, 0);
   load_rh(0);
   store_tile(0);
 
@@ -208,19 +229,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int tr_row = 4 * (grp >> 1) + (jl >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
 
+  int kh0 = 0, kw0 = 0;  // this tile
   for (int t = 0; t < T; ++t) {
     __syncthreads();
     const int buf = t & 1;
-    const int tb = t / nHt;
-    if (t == tb * nHt) load_band(tb * kTileCols);
+    if (kh0 == 0) load_band(kw0);
     float rh[QT][4];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) rh[qt][r] = rhn[qt][r];
+    int nkh = kh0 + kTileRows, nkw = kw0;  // next tile
+    if (nkh >= H) {
+      nkh = 0;
+      nkw += kTileCols;
+    }
     if (t + 1 < T) {
-      load_tile(t + 1);
-      load_rh(t + 1);
+      load_tile(nkh, nkw);
+      load_rh(nkh);
     }
     const uint16_t* kb = Ks + buf * kTileHalves;
     const uint16_t* vb = Vs + buf * kTileHalves;
@@ -334,6 +360,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
 
     if (t + 1 < T) store_tile(buf ^ 1);
+    kh0 = nkh;
+    kw0 = nkw;
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
