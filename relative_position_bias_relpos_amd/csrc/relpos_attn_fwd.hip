@@ -15,13 +15,21 @@
 //     o = 32*st + 8*g + 4*(lane/32) + e, i.e. grid offsets r = 2*st + g/2 and
 //     c = 8*(g%2) + 4*(lane/32) + e.  Its bias therefore needs 8 rel_w values
 //     per column band (kept in registers for the whole band) and 4 rel_h
-//     values per tile (prefetched from global memory one tile ahead).  LDS
-//     holds only the double-buffered K/V tiles.
+//     values per tile (prefetched from global memory one tile ahead).
 //   * O^T += V^T * P^T, again 32x32x16 MFMA, with P in fp16.  V tiles are kept
 //     row-major in LDS and read with the gfx950 transpose read
 //     (ds_read_b64_tr_b16), which hands each lane four consecutive keys of one
 //     V column.  bf16 V is converted to fp16 while staging (exact for
 //     |v| < 65520).
+//
+// Pipeline (one barrier per tile)
+//   * K/V tiles live in a 4-slot LDS ring.  In step t a wave issues, in one
+//     basic block, the Q.K^T MFMAs of tile t+1 (slot (t+1)%4), the softmax of
+//     tile t and the P.V MFMAs of tile t-1 (slot (t-1)%4), interleaved so the
+//     matrix cores run while the VALU does exp/convert work.  Then it stores
+//     the registers holding tile t+2 into slot (t+2)%4 and starts the global
+//     loads of tile t+3.  The loop is unrolled by two with the S and P register
+//     sets swapping roles, so no copies are made between steps.
 //
 // Online softmax (exp2 domain, scores pre-multiplied by log2 e)
 //   * Each query row keeps a reference maximum m.  Per tile,
@@ -33,6 +41,8 @@
 //     rescaled by exp2(m_old - m_new), and the tile's p are recomputed.  Between
 //     such events no rescale of O is needed; p stays <= 2^15 (finite in fp16)
 //     and the row's first maximum keeps l >= 1.
+#include <type_traits>
+
 #include "relpos_device.hpp"
 #include "relpos_kernels.hpp"
 
@@ -46,6 +56,7 @@ constexpr int kTileRows = 4;
 constexpr int kTileCols = 16;
 constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
 constexpr int kTileHalves = kTileKeys * kKStride;
+constexpr int kSlots = 4;               // LDS ring depth (power of two)
 constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
@@ -85,8 +96,21 @@ __device__ __forceinline__ int xcd_work_index(int G) {
   return start + (L >> 3);
 }
 
+struct TilePos {
+  int kh, kw;
+};
+
+__device__ __forceinline__ TilePos next_tile(TilePos p, int H) {
+  p.kh += kTileRows;
+  if (p.kh >= H) {
+    p.kh = 0;
+    p.kw += kTileCols;
+  }
+  return p;
+}
+
 template <bool BF16, bool OUT_F32, int NW, int QT>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
+__global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
@@ -96,16 +120,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int N = H * W;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [2][64][kKStride]
-  uint16_t* Vs = Ks + 2 * kTileHalves;                // [2][64][kKStride]
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [kSlots][64][kKStride]
+  uint16_t* Vs = Ks + kSlots * kTileHalves;          // [kSlots][64][kKStride]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
 
-  const int G = static_cast<int>(gridDim.x);
-  const int work = xcd_work_index(G);
+  const int work = xcd_work_index(static_cast<int>(gridDim.x));
   const int bh = work / q_tiles;
   const int q0 = (work - bh * q_tiles) * BM;
   const size_t head = static_cast<size_t>(bh) * N;
@@ -124,9 +147,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
   }
 
-  const int nWt = (W + kTileCols - 1) / kTileCols;
-  const int nHt = (H + kTileRows - 1) / kTileRows;
-  const int T = nWt * nHt;
+  const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
 
   // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
   constexpr int CH = (kTileKeys * kD / 8) / NT;  // 16-byte chunks of K (and of V) per thread
@@ -147,20 +168,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head * kD, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head * kD, head_bytes);
 
-  // Tile t covers grid rows [kh0, kh0+4) and columns [kw0, kw0+16).
-  auto load_tile = [&](int kh0, int kw0) {
-    const int base = kh0 * W + kw0;
+  auto load_tile = [&](TilePos p) {
+    const int base = p.kh * W + p.kw;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
-      const bool ok = (kh0 + ch_r[s] < H) && (kw0 + ch_c[s] < W);
+      const bool ok = (p.kh + ch_r[s] < H) && (p.kw + ch_c[s] < W);
       const int off = ok ? ((base + ch_off[s]) * kD + dcol) * 2 : kOob;
       kreg[s] = buf_load16(krs, off);
       vreg[s] = buf_load16(vrs, off);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* kb = Ks + buf * kTileHalves;
-    uint16_t* vb = Vs + buf * kTileHalves;
+  auto store_tile = [&](int slot) {
+    uint16_t* kb = Ks + slot * kTileHalves;
+    uint16_t* vb = Vs + slot * kTileHalves;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
       *reinterpret_cast<u32x4*>(kb + ch_lds[s]) = kreg[s];
@@ -173,8 +193,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
   };
 
-  // rel_w' (x log2 e) for the lane's 8 key columns of a band and rel_h' for
-  // the 4 grid rows of a tile; -inf outside the grid.
+  // ---- bias: rel_w' (x log2 e) for the lane's 8 key columns of a band and
+  // rel_h' for the 4 grid rows of a tile; -inf outside the grid.
   const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
   const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
   int rw_off[QT], rh_off[QT];
@@ -206,11 +226,58 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       }
   };
 
-  load_tile(0, 0);
-  load_rh(0);
-  store_tile(0);
-
+  // ---- tile compute pieces -----------------------------------------------
+  // S^T = K Q^T for the tile in `slot` (two 32-key halves per query tile).
+  auto qk = [&](int slot, f32x16 (&s)[QT][2]) {
+    const uint16_t* kb = Ks + slot * kTileHalves;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt][st] = f32x16{};
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32<BF16>(kf, qf[qt][kd], s[qt][st]);
+      }
+    }
+  };
+  // transpose-read lane addressing for the V^T operand
+  const int grp = lane >> 4, jl = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (jl >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
   f32x16 acc[QT][2];
+  // O^T += V^T P^T for the tile in `slot`: four 16-key steps, two 32-row d tiles.
+  auto pv = [&](int slot, const u32x4 (&pf)[QT][4]) {
+    const uint16_t* vb = Vs + slot * kTileHalves;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
+        const u32x2 lo = ds_read_tr16(vp);
+        const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf, pf[qt][ks], acc[qt][dt]);
+      }
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 in LDS, tile 2 in registers, S of tile 0 ----
+  const TilePos p0{0, 0};
+  const TilePos p1 = next_tile(p0, H);
+  const TilePos p2 = next_tile(p1, H);
+  load_tile(p0);
+  store_tile(0);
+  if (T > 1) {
+    load_tile(p1);
+    store_tile(1);
+  }
+  if (T > 2) load_tile(p2);
+  load_rh(0);
+  __syncthreads();
+
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     acc[t][0] = f32x16{};
@@ -224,97 +291,119 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // transpose-read lane addressing for the V^T operand (see header comment)
-  const int grp = lane >> 4, jl = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (jl >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
+  f32x16 sA[QT][2], sB[QT][2];
+  u32x4 pA[QT][4], pB[QT][4];
+  qk(0, sA);
 
-  int kh0 = 0, kw0 = 0;  // this tile
-  for (int t = 0; t < T; ++t) {
-    __syncthreads();
-    const int buf = t & 1;
-    if (kh0 == 0) load_band(kw0);
+  TilePos pc = p0;                // tile t
+  TilePos pl = next_tile(p2, H);  // tile t+3, the next one to load
+
+  // One pipeline step for tile t: Q.K^T of tile t+1 (into sn), softmax of
+  // tile t (sc -> pcur) and P.V of tile t-1 (pprev), all in one basic block so
+  // the MFMA and VALU streams interleave; then the rare maximum move, the
+  // staging of tile t+2 and one barrier.
+  auto step = [&](int t, auto first_c, auto last_c, f32x16 (&sc)[QT][2], f32x16 (&sn)[QT][2],
+                  u32x4 (&pprev)[QT][4], u32x4 (&pcur)[QT][4]) {
+    constexpr bool kFirst = decltype(first_c)::value;
+    constexpr bool kLast = decltype(last_c)::value;
+    if (pc.kh == 0) load_band(pc.kw);
     float rh[QT][4];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) rh[qt][r] = rhn[qt][r];
-    int nkh = kh0 + kTileRows, nkw = kw0;  // next tile
-    if (nkh >= H) {
-      nkh = 0;
-      nkw += kTileCols;
-    }
-    if (t + 1 < T) {
-      load_tile(nkh, nkw);
-      load_rh(nkh);
-    }
-    const uint16_t* kb = Ks + buf * kTileHalves;
-    const uint16_t* vb = Vs + buf * kTileHalves;
+    const TilePos pn = next_tile(pc, H);
+    if constexpr (!kLast) load_rh(pn.kh);
 
-    // K^T fragments are shared by this wave's query tiles.
-    u32x4 kf[2][4];
+    // Operands of this step's MFMAs: K^T fragments of tile t+1 and V^T
+    // fragments of tile t-1, read from LDS two chunks ahead of their use.
+    const uint16_t* kb = Ks + ((t + 1) & (kSlots - 1)) * kTileHalves;
+    const uint16_t* vb = Vs + ((t - 1) & (kSlots - 1)) * kTileHalves;
+    auto read_k = [&](int i) -> u32x4 {
+      const int st = i & 1, kd = i >> 1;
+      return *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
+    };
+    auto read_v = [&](int i) -> u32x4 {
+      const int dt = i & 1, ks = i >> 1;
+      const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
+      const u32x2 lo = ds_read_tr16(vp);
+      const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 kf[8], vf[8];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kd = 0; kd < 4; ++kd)
-        kf[st][kd] = *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (!kLast) kf[i] = read_k(i);
+      if constexpr (!kFirst) vf[i] = read_v(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    u32x4 pf[QT][4];
+    // Eight chunks, each: one Q.K^T MFMA of tile t+1, one P.V MFMA of tile
+    // t-1 and the softmax of four of tile t's scores per query tile.  The
+    // fences keep this order so the matrix cores run under the VALU work.
     float tsum[QT];
-    f32x16 s[QT][2];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) tsum[qt] = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[qt][st] = f32x16{};
-#pragma unroll
-        for (int kd = 0; kd < 4; ++kd) s[qt][st] = mfma32<BF16>(kf[st][kd], qf[qt][kd], s[qt][st]);
+    for (int i = 0; i < 8; ++i) {
+      if (i + 2 < 8) {
+        if constexpr (!kLast) kf[i + 2] = read_k(i + 2);
+        if constexpr (!kFirst) vf[i + 2] = read_v(i + 2);
       }
-    }
-
-    bool grow = (t == 0);
+      if constexpr (!kLast) {
+        const int st = i & 1, kd = i >> 1;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float ts = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float rhm = rh[qt][2 * st + (g >> 1)] - m[qt];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float b = rw[qt][4 * (g & 1) + e] + rhm;
-            s[qt][st][4 * g + e] = __builtin_fmaf(s[qt][st][4 * g + e], c2, b);
-          }
-        }
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          uint32_t w4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            w4[i] = pack_f16(exp2_fast(s[qt][st][8 * gg + 2 * i]), exp2_fast(s[qt][st][8 * gg + 2 * i + 1]));
-            ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
-          }
-          pf[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        for (int qt = 0; qt < QT; ++qt) {
+          sn[qt][st] = mfma32<BF16>(kf[i], qf[qt][kd], kd == 0 ? f32x16{} : sn[qt][st]);
         }
       }
-      tsum[qt] = ts;
-      grow = grow || !(ts <= kGrowLimit);
+      if constexpr (!kFirst) {
+        const int dt = i & 1, ks = i >> 1;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf[i], pprev[qt][ks], acc[qt][dt]);
+      }
+      // scores 4*i .. 4*i+3 of the lane: st = i/4, g = i%4
+      const int st = i >> 2, g = i & 3;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float rhm = rh[qt][2 * st + (g >> 1)] - m[qt];
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float b = rw[qt][4 * (g & 1) + e] + rhm;
+          x[e] = __builtin_fmaf(sc[qt][st][4 * g + e], c2, b);
+          sc[qt][st][4 * g + e] = x[e];
+        }
+        const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
+        const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
+        tsum[qt] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum[qt], false);
+        tsum[qt] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum[qt], false);
+        // registers 8*gg + 2*j of S tile st map to P operand (2*st + gg), word j
+        pcur[qt][2 * st + (g >> 1)][2 * (g & 1)] = w0;
+        pcur[qt][2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    bool grow = kFirst;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) grow = grow || !(tsum[qt] <= kGrowLimit);
 
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       // Move the reference maximum: exact tile maximum per query, then
-      // rescale O and l and recompute this tile's p against the new m.
+      // rescale O (which already holds tiles < t) and l, and recompute this
+      // tile's p against the new m.  (The empty volatile asm keeps this rare
+      // block a real branch instead of code speculated on every tile.)
+      __asm__ volatile("; reference maximum moves" ::);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         float mx = -__builtin_inff();
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qt][st][r]);
+          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[qt][st][r]);
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
         float inc;
-        if (t == 0) {
+        if (kFirst) {
           inc = mx;  // O and l are still zero: only set m
         } else {
           inc = __builtin_fmaxf(mx, 0.f);
@@ -332,36 +421,49 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
             uint32_t w4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              w4[i] = pack_f16(exp2_fast(s[qt][st][8 * gg + 2 * i] - inc),
-                               exp2_fast(s[qt][st][8 * gg + 2 * i + 1] - inc));
+              w4[i] = pack_f16(exp2_fast(sc[qt][st][8 * gg + 2 * i] - inc),
+                               exp2_fast(sc[qt][st][8 * gg + 2 * i + 1] - inc));
               ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
             }
-            pf[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+            pcur[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
           }
         }
         tsum[qt] = ts;
       }
     }
-
-    // O^T += V^T P^T: four 16-key steps, two 32-row d tiles.
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l[qt] += tsum[qt];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
-        const u32x2 lo = ds_read_tr16(vp);
-        const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
-        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf, pf[qt][ks], acc[qt][dt]);
-      }
-    }
 
-    if (t + 1 < T) store_tile(buf ^ 1);
-    kh0 = nkh;
-    kw0 = nkw;
+    // tile t+2: registers -> LDS slot (t+2)%4 (last read in iteration t-1);
+    // then start the global loads of tile t+3.
+    if (t + 2 < T) store_tile((t + 2) & (kSlots - 1));
+    if (t + 3 < T) load_tile(pl);
+    __syncthreads();
+    pl = next_tile(pl, H);
+    pc = pn;
+  };
+
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  const int slot_last = (T - 1) & (kSlots - 1);
+  if (T == 1) {
+    step(0, True{}, True{}, sA, sB, pB, pA);
+    pv(slot_last, pA);
+  } else {
+    step(0, True{}, False{}, sA, sB, pB, pA);
+    int t = 1;
+    for (; t + 2 < T; t += 2) {
+      step(t, False{}, False{}, sB, sA, pA, pB);
+      step(t + 1, False{}, False{}, sA, sB, pB, pA);
+    }
+    if (t + 2 == T) {
+      step(t, False{}, False{}, sB, sA, pA, pB);
+      step(t + 1, False{}, True{}, sA, sB, pB, pA);
+      pv(slot_last, pA);
+    } else {
+      step(t, False{}, True{}, sB, sA, pA, pB);
+      pv(slot_last, pB);
+    }
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
@@ -411,22 +513,19 @@ hipError_t launch_dt(const AttnArgs& a, int cfg, size_t lds, hipStream_t stream)
   switch (cfg) {
     case 0: return launch_cfg<BF16, OUT_F32, 4, 1>(a, lds, stream);
     case 1: return launch_cfg<BF16, OUT_F32, 2, 1>(a, lds, stream);
-    case 2: return launch_cfg<BF16, OUT_F32, 1, 1>(a, lds, stream);
-    case 3: return launch_cfg<BF16, OUT_F32, 4, 2>(a, lds, stream);
-    default: return launch_cfg<BF16, OUT_F32, 2, 2>(a, lds, stream);
+    default: return launch_cfg<BF16, OUT_F32, 1, 1>(a, lds, stream);
   }
 }
 
-
 }  // namespace
 
-int attn_num_configs() { return 5; }
+int attn_num_configs() { return 3; }
 
 size_t attn_lds_bytes(int cfg, int H, int W) {
   (void)cfg;
   (void)H;
   (void)W;
-  return 2 * 2 * static_cast<size_t>(kTileHalves) * 2;  // K and V, double-buffered
+  return 2 * kSlots * static_cast<size_t>(kTileHalves) * 2;  // K and V, kSlots-deep ring
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {

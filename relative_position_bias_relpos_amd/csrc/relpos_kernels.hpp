@@ -34,8 +34,8 @@ struct AttnArgs {
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
-// Attention launch configurations (waves per workgroup x 32-query tiles per
-// wave): 0: 4x1, 1: 2x1, 2: 1x1, 3: 4x2, 4: 2x2.
+// Attention launch configurations (waves per workgroup, 32 queries per wave):
+// 0: 4 waves, 1: 2 waves, 2: 1 wave.
 int attn_num_configs();
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
