@@ -57,6 +57,10 @@ constexpr int kTileCols = 16;
 constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
 constexpr int kTileHalves = kTileKeys * kKStride;
 constexpr int kSlots = 4;               // LDS ring depth (power of two)
+#ifndef RELPOS_CHUNKS_PER_FENCE
+#define RELPOS_CHUNKS_PER_FENCE 8
+#endif
+constexpr int kChunksPerFence = RELPOS_CHUNKS_PER_FENCE;  // MFMA/VALU chunks between scheduling fences
 constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
@@ -307,13 +311,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
     constexpr bool kFirst = decltype(first_c)::value;
     constexpr bool kLast = decltype(last_c)::value;
     if (pc.kh == 0) load_band(pc.kw);
-    float rh[QT][4];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rh[qt][r] = rhn[qt][r];
     const TilePos pn = next_tile(pc, H);
-    if constexpr (!kLast) load_rh(pn.kh);
 
     // Operands of this step's MFMAs: K^T fragments of tile t+1 and V^T
     // fragments of tile t-1, read from LDS two chunks ahead of their use.
@@ -366,7 +364,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
       const int st = i >> 2, g = i & 3;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float rhm = rh[qt][2 * st + (g >> 1)] - m[qt];
+        const float rhm = rhn[qt][2 * st + (g >> 1)] - m[qt];
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -382,8 +380,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
         pcur[qt][2 * st + (g >> 1)][2 * (g & 1)] = w0;
         pcur[qt][2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if ((i + 1) % kChunksPerFence == 0) __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!kLast) load_rh(pn.kh);  // rel_h' of tile t+1 (this tile's values are used)
+
+    // tile t+2: registers -> LDS slot (t+2)%4 (last read in iteration t-1);
+    // then start the global loads of tile t+3.
+    if (t + 2 < T) store_tile((t + 2) & (kSlots - 1));
+    if (t + 3 < T) load_tile(pl);
     bool grow = kFirst;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) grow = grow || !(tsum[qt] <= kGrowLimit);
@@ -434,10 +438,6 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l[qt] += tsum[qt];
 
-    // tile t+2: registers -> LDS slot (t+2)%4 (last read in iteration t-1);
-    // then start the global loads of tile t+3.
-    if (t + 2 < T) store_tile((t + 2) & (kSlots - 1));
-    if (t + 3 < T) load_tile(pl);
     __syncthreads();
     pl = next_tile(pl, H);
     pc = pn;
