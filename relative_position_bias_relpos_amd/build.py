@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librelpos.so")
-SOURCES = ["relpos_api.hip", "relpos_build.hip", "relpos_attn_fwd.hip"]
+SOURCES = ["relpos_api.hip", "relpos_build.hip", "relpos_attn_fwd.hip", "relpos_attn16.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [

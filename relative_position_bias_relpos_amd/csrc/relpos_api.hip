@@ -100,9 +100,9 @@ int device_lds_limit(int* out) {
 }
 
 // Order in which attention configurations are tried (first that fits LDS).
-constexpr int kAttnPreference[] = {0, 1, 2};
+constexpr int kAttnPreference[] = {0, 1, 2, 3, 4};
 
-// Tuning knob: RELPOS_ATTN_CFG=<0..2> forces one configuration when it fits
+// Tuning knob: RELPOS_ATTN_CFG=<0..4> forces one configuration when it fits
 // (read on every call, so one process can compare configurations).
 int forced_attn_config() {
   const char* e = std::getenv("RELPOS_ATTN_CFG");

@@ -1,0 +1,352 @@
+// relpos_attn_fwd, 16-query-per-wave kernel (launch configurations 3 and 4).
+//
+// Same method as the 32-query kernel in relpos_attn_fwd.hip (PR #55629 page,
+// implementation section, item 1: K/V streamed with an online softmax and the
+// rel_h/rel_w slices added per key block), laid out for more waves per SIMD:
+//
+//   * A wave owns 16 queries; a workgroup of NW waves owns 16*NW queries of one
+//     (batch, head).  With NW = 4 a workgroup covers 64 queries (three per CU
+//     on a 64x64 grid with 12 heads) and three waves fit per SIMD.  Measured on
+//     MI355X it is slower than the 32-query kernel on every workload here (twice
+//     the LDS operand traffic per score, and 16x16 MFMAs hide less VALU work),
+//     so it is not the default.
+//   * S^T = K Q^T on 16x16x32 MFMA.  A lane holds one query (lane%16) and, per
+//     64-key tile of the key grid (4 rows x 16 columns), 16 keys
+//     o = 16*st + 4*g + j (g = lane/16), i.e. grid row st and grid column
+//     4*g + j.  Its bias needs 4 rel_w values per 16-column band and 4 rel_h
+//     values per tile.
+//   * O^T += V^T P^T on 16x16x32 MFMA with P in fp16.  For the 32-key step ks
+//     the lane's 8 P values are keys 32ks + 4g + {0..3} and 32ks + 16 + 4g +
+//     {0..3}; the V^T operand is two transpose reads of four consecutive keys.
+//   * Two-stage pipeline: step t issues Q.K^T of tile t+1 together with the
+//     softmax of tile t, then P.V of tile t.  K lives in a 2-slot LDS ring and
+//     V in a 3-slot ring (tile t+2 is staged while t and t+1 are resident).
+//   * Online softmax with a lazy reference maximum, as in the 32-query kernel:
+//     m moves only on the first tile or when a tile's rounded-p sum exceeds
+//     2^15; the row sum adds the rounded fp16 p.
+#include <type_traits>
+
+#include "relpos_attn_common.hpp"
+#include "relpos_kernels.hpp"
+
+namespace relpos {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kKSlots16 = 2;
+constexpr int kVSlots16 = 3;
+
+template <bool BF16, bool OUT_F32, int NW>
+__global__ __launch_bounds__(NW * 64, NW <= 4 ? 3 : 2) void attn16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
+    const float* __restrict__ rel_w, void* __restrict__ out,
+    int H, int W, int q_tiles, float c2) {
+  constexpr int BM = 16 * NW;
+  constexpr int NT = NW * 64;
+  const int N = H * W;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [2][64][kKStride]
+  uint16_t* Vs = Ks + kKSlots16 * kTileHalves;       // [3][64][kKStride]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = lane >> 4;   // lane group: which 4 keys of each 16-key row, which 8 k of an MFMA
+  const int col = lane & 15;   // this lane's query within the wave
+
+  const int work = xcd_work_index(static_cast<int>(gridDim.x));
+  const int bh = work / q_tiles;
+  const int q0 = (work - bh * q_tiles) * BM;
+  const size_t head = static_cast<size_t>(bh) * N;
+
+  // ---- Q^T operand fragments: d = 32*kd + 8*grp .. +7 ------------------------
+  const int qrow = wave * 16 + col;
+  const int qi = q0 + qrow;
+  u32x4 qf[2];
+#pragma unroll
+  for (int kd = 0; kd < 2; ++kd) {
+    qf[kd] = (qi < N) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 32 * kd + 8 * grp)
+                      : u32x4{0, 0, 0, 0};
+  }
+
+  const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
+
+  // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
+  constexpr int CH = (kTileKeys * kD / 8) / NT;
+  static_assert(CH >= 1, "workgroup too large for one tile");
+  int ch_r[CH], ch_c[CH], ch_off[CH], ch_lds[CH];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    const int cid = tid + s * NT;
+    const int o = cid >> 3, dc = cid & 7;
+    ch_r[s] = o >> 4;
+    ch_c[s] = o & 15;
+    ch_off[s] = (o >> 4) * W + (o & 15);
+    ch_lds[s] = o * kKStride + 8 * dc;
+  }
+  const int dcol = 8 * (tid & 7);
+  u32x4 kreg[CH], vreg[CH];
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head * kD, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head * kD, head_bytes);
+
+  auto load_tile = [&](TilePos p) {
+    const int base = p.kh * W + p.kw;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      const bool ok = (p.kh + ch_r[s] < H) && (p.kw + ch_c[s] < W);
+      const int off = ok ? ((base + ch_off[s]) * kD + dcol) * 2 : kOob;
+      kreg[s] = buf_load16(krs, off);
+      vreg[s] = buf_load16(vrs, off);
+    }
+  };
+  auto store_tile = [&](int kslot, int vslot) {
+    uint16_t* kb = Ks + kslot * kTileHalves;
+    uint16_t* vb = Vs + vslot * kTileHalves;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      *reinterpret_cast<u32x4*>(kb + ch_lds[s]) = kreg[s];
+      u32x4 x = vreg[s];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x[w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
+      }
+      *reinterpret_cast<u32x4*>(vb + ch_lds[s]) = x;
+    }
+  };
+
+  // ---- bias: rel_w' for the lane's 4 columns of a band, rel_h' per tile ------
+  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
+  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
+  const int rw_off = (qi < N ? qi : 0) * W * 4;
+  const int rh_off = (qi < N ? qi : 0) * H * 4;
+  float rw[4];
+  auto load_band = [&](int kw0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = kw0 + 4 * grp + j;
+      const float x = buf_loadf(rwrs, c < W ? rw_off + 4 * c : kOob);
+      rw[j] = (c < W) ? x * kLog2e : -__builtin_inff();
+    }
+  };
+  float rhn[4];  // rel_h' of the 4 grid rows of the next tile to process
+  auto load_rh = [&](int kh0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = buf_loadf(rhrs, kh0 + r < H ? rh_off + 4 * (kh0 + r) : kOob);
+      rhn[r] = (kh0 + r < H) ? x * kLog2e : -__builtin_inff();
+    }
+  };
+
+  // ---- compute pieces ------------------------------------------------------
+  auto qk = [&](int kslot, f32x4 (&s)[4]) {
+    const uint16_t* kb = Ks + kslot * kTileHalves;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kb + (16 * st + col) * kKStride + 8 * grp);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kb + (16 * st + col) * kKStride + 32 + 8 * grp);
+      s[st] = mfma16<BF16>(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      s[st] = mfma16<BF16>(k1, qf[1], s[st]);
+    }
+  };
+  const int jl = col;
+  const int tr_row = 4 * grp + (jl >> 2);
+  const int tr_col = 4 * (jl & 3);
+  f32x4 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto pv = [&](int vslot, const u32x4 (&pf)[2]) {
+    const uint16_t* vb = Vs + vslot * kTileHalves;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t* vp = vb + (32 * ks + tr_row) * kKStride + 16 * dt + tr_col;
+        const u32x2 lo = ds_read_tr16(vp);
+        const u32x2 hi = ds_read_tr16(vp + 16 * kKStride);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+        acc[dt] = mfma16<false>(vf, pf[ks], acc[dt]);
+      }
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 in LDS, tile 2 in registers ------------------
+  const TilePos p0{0, 0};
+  const TilePos p1 = next_tile(p0, H);
+  const TilePos p2 = next_tile(p1, H);
+  load_tile(p0);
+  store_tile(0, 0);
+  if (T > 1) {
+    load_tile(p1);
+    store_tile(1, 1);
+  }
+  if (T > 2) load_tile(p2);
+  load_rh(0);
+  __syncthreads();
+
+  float m = 0.f, l = 0.f;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  f32x4 sA[4], sB[4];
+  qk(0, sA);
+
+  TilePos pc = p0;                // tile t
+  TilePos pl = next_tile(p2, H);  // tile t+3
+  int vslot = 0;                  // t % 3
+
+  auto step = [&](int t, auto first_c, auto last_c, f32x4 (&sc)[4], f32x4 (&sn)[4]) {
+    constexpr bool kFirst = decltype(first_c)::value;
+    constexpr bool kLast = decltype(last_c)::value;
+    if (pc.kh == 0) load_band(pc.kw);
+    const TilePos pn = next_tile(pc, H);
+    if constexpr (!kLast) qk((t + 1) & 1, sn);
+
+    // softmax of tile t against the current reference maximum
+    u32x4 pf[2];
+    float tsum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const float rhm = rhn[st] - m;
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = __builtin_fmaf(sc[st][j], c2, rw[j] + rhm);
+        sc[st][j] = x[j];
+      }
+      const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
+      const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum, false);
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum, false);
+      pf[st >> 1][2 * (st & 1)] = w0;
+      pf[st >> 1][2 * (st & 1) + 1] = w1;
+    }
+    if constexpr (!kLast) load_rh(pn.kh);
+
+    const bool grow = kFirst || !(tsum <= kGrowLimit);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // Move the reference maximum: exact tile maximum per query (over the
+      // four lane groups holding it), rescale O and l, recompute this tile's p.
+      // (The empty volatile asm keeps this rare block a real branch.)
+      __asm__ volatile("; reference maximum moves" ::);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, sc[st][j]);
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      float inc;
+      if (kFirst) {
+        inc = mx;  // O and l are still zero: only set m
+      } else {
+        inc = __builtin_fmaxf(mx, 0.f);
+        const float alpha = exp2_fast(-inc);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      }
+      m += inc;
+      tsum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint32_t w0 = pack_f16(exp2_fast(sc[st][0] - inc), exp2_fast(sc[st][1] - inc));
+        const uint32_t w1 = pack_f16(exp2_fast(sc[st][2] - inc), exp2_fast(sc[st][3] - inc));
+        tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum, false);
+        tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum, false);
+        pf[st >> 1][2 * (st & 1)] = w0;
+        pf[st >> 1][2 * (st & 1) + 1] = w1;
+      }
+    }
+    l += tsum;
+
+    pv(vslot, pf);
+
+    // tile t+2 -> K slot (t+2)%2, V slot (t+2)%3; start the loads of tile t+3
+    const int vslot2 = (vslot == 0) ? 2 : vslot - 1;  // (t+2) % 3
+    // K slot t%2 held tile t, read by Q.K^T(t) in the previous step (or, for
+    // t = 0, in the prologue, which no barrier separates from this store).
+    if constexpr (kFirst) __syncthreads();
+    if (t + 2 < T) store_tile(t & 1, vslot2);
+    if (t + 3 < T) load_tile(pl);
+    __syncthreads();
+    pl = next_tile(pl, H);
+    pc = pn;
+    vslot = (vslot == 2) ? 0 : vslot + 1;
+  };
+
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  if (T == 1) {
+    step(0, True{}, True{}, sA, sB);
+  } else {
+    step(0, True{}, False{}, sA, sB);
+    int t = 1;
+    for (; t + 2 < T; t += 2) {
+      step(t, False{}, False{}, sB, sA);
+      step(t + 1, False{}, False{}, sA, sB);
+    }
+    if (t + 2 == T) {
+      step(t, False{}, False{}, sB, sA);
+      step(t + 1, False{}, True{}, sA, sB);
+    } else {
+      step(t, False{}, True{}, sB, sA);
+    }
+  }
+
+  // ---- epilogue: sum l over the four lane groups, normalise, store --------
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (qi < N) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 16 * dt + 4 * grp;
+      const f32x4 o4 = acc[dt] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
+      } else {
+        const u32x2 pk = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
+                              : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (head + qi) * kD + d) = pk;
+      }
+    }
+  }
+}
+
+template <bool BF16, bool OUT_F32, int NW>
+hipError_t launch16(const AttnArgs& a, hipStream_t stream) {
+  auto kern = attn16_kernel<BF16, OUT_F32, NW>;
+  const size_t lds = attn16_lds_bytes();
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (err != hipSuccess) return err;
+  constexpr int BM = 16 * NW;
+  const int q_tiles = (a.H * a.W + BM - 1) / BM;
+  dim3 grid(static_cast<unsigned>(q_tiles * a.BH));
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
+                     a.H, a.W, q_tiles, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool OUT_F32>
+hipError_t launch16_nw(const AttnArgs& a, int nw, hipStream_t stream) {
+  return nw == 8 ? launch16<BF16, OUT_F32, 8>(a, stream) : launch16<BF16, OUT_F32, 4>(a, stream);
+}
+
+}  // namespace
+
+size_t attn16_lds_bytes() { return static_cast<size_t>(kKSlots16 + kVSlots16) * kTileHalves * 2; }
+
+hipError_t launch_attn16(const AttnArgs& a, int nw, hipStream_t stream) {
+  if (a.bf16) {
+    return a.out_f32 ? launch16_nw<true, true>(a, nw, stream) : launch16_nw<true, false>(a, nw, stream);
+  }
+  return a.out_f32 ? launch16_nw<false, true>(a, nw, stream) : launch16_nw<false, false>(a, nw, stream);
+}
+
+}  // namespace relpos

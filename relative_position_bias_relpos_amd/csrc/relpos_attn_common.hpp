@@ -1,0 +1,73 @@
+// Device helpers shared by the attention kernels (gfx950).
+#pragma once
+
+#include "relpos_device.hpp"
+
+namespace relpos {
+namespace attn {
+
+constexpr int kD = 64;
+constexpr int kTileKeys = 64;
+constexpr int kTileRows = 4;
+constexpr int kTileCols = 16;
+constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
+constexpr int kTileHalves = kTileKeys * kKStride;
+constexpr int kSlots = 4;               // LDS ring depth (power of two)
+#ifndef RELPOS_CHUNKS_PER_FENCE
+#define RELPOS_CHUNKS_PER_FENCE 8
+#endif
+constexpr int kChunksPerFence = RELPOS_CHUNKS_PER_FENCE;  // MFMA/VALU chunks between scheduling fences
+constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
+
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read.  Within each 16-lane group, lane i receives
+// element (i % 4) of the 4-element row addressed by lane 4*k + i/4, k = 0..3.
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Raw buffer loads: an offset at or past the resource's byte size returns
+// zeros in hardware, which masks grid cells outside the tile without branches.
+constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw-buffer descriptor word 3
+constexpr int kOob = 0x7ffffff0;             // any offset past every resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                          static_cast<int>(kBufFlags));
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Logical work index of this workgroup.  Workgroups are dispatched round-robin
+// over the 8 XCDs; this maps the blocks that land on one XCD to a contiguous
+// range of (head, query tile) work so that a head's K/V stays in one XCD's L2.
+__device__ __forceinline__ int xcd_work_index(int G) {
+  const int L = blockIdx.x;
+  const int xcd = L & 7;
+  const int per = G >> 3, rem = G & 7;
+  const int start = xcd * per + (xcd < rem ? xcd : rem);
+  return start + (L >> 3);
+}
+
+struct TilePos {
+  int kh, kw;
+};
+
+__device__ __forceinline__ TilePos next_tile(TilePos p, int H) {
+  p.kh += kTileRows;
+  if (p.kh >= H) {
+    p.kh = 0;
+    p.kw += kTileCols;
+  }
+  return p;
+}
+
+}  // namespace attn
+}  // namespace relpos

@@ -43,75 +43,14 @@
 //     and the row's first maximum keeps l >= 1.
 #include <type_traits>
 
-#include "relpos_device.hpp"
+#include "relpos_attn_common.hpp"
 #include "relpos_kernels.hpp"
 
 namespace relpos {
 
 namespace {
 
-constexpr int kD = 64;
-constexpr int kTileKeys = 64;
-constexpr int kTileRows = 4;
-constexpr int kTileCols = 16;
-constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
-constexpr int kTileHalves = kTileKeys * kKStride;
-constexpr int kSlots = 4;               // LDS ring depth (power of two)
-#ifndef RELPOS_CHUNKS_PER_FENCE
-#define RELPOS_CHUNKS_PER_FENCE 8
-#endif
-constexpr int kChunksPerFence = RELPOS_CHUNKS_PER_FENCE;  // MFMA/VALU chunks between scheduling fences
-constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
-
-typedef short __attribute__((ext_vector_type(4))) s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// gfx950 LDS transpose read.  Within each 16-lane group, lane i receives
-// element (i % 4) of the 4-element row addressed by lane 4*k + i/4, k = 0..3.
-__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// Raw buffer loads: an offset at or past the resource's byte size returns
-// zeros in hardware, which masks grid cells outside the tile without branches.
-constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw-buffer descriptor word 3
-constexpr int kOob = 0x7ffffff0;             // any offset past every resource used here
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                          static_cast<int>(kBufFlags));
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
-// Logical work index of this workgroup.  Workgroups are dispatched round-robin
-// over the 8 XCDs; this maps the blocks that land on one XCD to a contiguous
-// range of (head, query tile) work so that a head's K/V stays in one XCD's L2.
-__device__ __forceinline__ int xcd_work_index(int G) {
-  const int L = blockIdx.x;
-  const int xcd = L & 7;
-  const int per = G >> 3, rem = G & 7;
-  const int start = xcd * per + (xcd < rem ? xcd : rem);
-  return start + (L >> 3);
-}
-
-struct TilePos {
-  int kh, kw;
-};
-
-__device__ __forceinline__ TilePos next_tile(TilePos p, int H) {
-  p.kh += kTileRows;
-  if (p.kh >= H) {
-    p.kh = 0;
-    p.kw += kTileCols;
-  }
-  return p;
-}
+using namespace attn;
 
 template <bool BF16, bool OUT_F32, int NW, int QT>
 __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
@@ -509,31 +448,34 @@ hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
 }
 
 template <bool BF16, bool OUT_F32>
-hipError_t launch_dt(const AttnArgs& a, int cfg, size_t lds, hipStream_t stream) {
-  switch (cfg) {
-    case 0: return launch_cfg<BF16, OUT_F32, 4, 1>(a, lds, stream);
-    case 1: return launch_cfg<BF16, OUT_F32, 2, 1>(a, lds, stream);
+hipError_t launch_dt(const AttnArgs& a, int nw, size_t lds, hipStream_t stream) {
+  switch (nw) {
+    case 4: return launch_cfg<BF16, OUT_F32, 4, 1>(a, lds, stream);
+    case 2: return launch_cfg<BF16, OUT_F32, 2, 1>(a, lds, stream);
     default: return launch_cfg<BF16, OUT_F32, 1, 1>(a, lds, stream);
   }
 }
 
+size_t attn32_lds_bytes() { return 2 * kSlots * static_cast<size_t>(kTileHalves) * 2; }
+
 }  // namespace
 
-int attn_num_configs() { return 3; }
+int attn_num_configs() { return 5; }
 
 size_t attn_lds_bytes(int cfg, int H, int W) {
-  (void)cfg;
   (void)H;
   (void)W;
-  return 2 * kSlots * static_cast<size_t>(kTileHalves) * 2;  // K and V, kSlots-deep ring
+  return cfg >= 3 ? attn16_lds_bytes() : attn32_lds_bytes();
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
-  const size_t lds = attn_lds_bytes(cfg, a.H, a.W);
+  if (cfg >= 3) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
+  const int nw = cfg == 0 ? 4 : (cfg == 1 ? 2 : 1);
+  const size_t lds = attn32_lds_bytes();
   if (a.bf16) {
-    return a.out_f32 ? launch_dt<true, true>(a, cfg, lds, stream) : launch_dt<true, false>(a, cfg, lds, stream);
+    return a.out_f32 ? launch_dt<true, true>(a, nw, lds, stream) : launch_dt<true, false>(a, nw, lds, stream);
   }
-  return a.out_f32 ? launch_dt<false, true>(a, cfg, lds, stream) : launch_dt<false, false>(a, cfg, lds, stream);
+  return a.out_f32 ? launch_dt<false, true>(a, nw, lds, stream) : launch_dt<false, false>(a, nw, lds, stream);
 }
 
 }  // namespace relpos

@@ -53,3 +53,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace relpos
+
+namespace relpos {
+
+// One 16x16x32 MFMA, C += A(16x32) * B(32x16), fp32 accumulate.  Each lane
+// holds 8 consecutive-k elements of A (row lane%16) and of B (column lane%16);
+// the lane group (lane/16) selects which 8 of the 32 k.  C: lane holds column
+// lane%16, rows 4*(lane/16) + 0..3.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+}  // namespace relpos

@@ -34,11 +34,17 @@ struct AttnArgs {
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
-// Attention launch configurations (waves per workgroup, 32 queries per wave):
-// 0: 4 waves, 1: 2 waves, 2: 1 wave.
+// Attention launch configurations:
+//   0, 1, 2: 32 queries per wave, 4, 2 or 1 waves per workgroup (default: 0)
+//   3: 16 queries per wave, 4 waves per workgroup (64 queries)
+//   4: 16 queries per wave, 8 waves per workgroup (128 queries)
 int attn_num_configs();
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
+
+// The 16-query-per-wave kernel (relpos_attn16.hip).
+size_t attn16_lds_bytes();
+hipError_t launch_attn16(const AttnArgs& a, int nw, hipStream_t stream);
 
 }  // namespace relpos
