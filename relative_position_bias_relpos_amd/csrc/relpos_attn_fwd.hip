@@ -52,13 +52,13 @@ namespace {
 
 using namespace attn;
 
-template <bool BF16, bool OUT_F32, int NW, int QT>
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED>
 __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int q_tiles, float c2) {
-  constexpr int BM = 32 * QT * NW;
+    int H, int W, int q_tiles, float c2, float rw_mul) {
+  constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
   const int N = H * W;
 
@@ -76,18 +76,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   const int q0 = (work - bh * q_tiles) * BM;
   const size_t head = static_cast<size_t>(bh) * N;
 
-  // ---- this lane's queries: Q^T operand fragments (4 k-steps of 16) -------
-  int qrow[QT];
-  u32x4 qf[QT][4];
+  // ---- this lane's query: Q^T operand fragments (4 k-steps of 16) ----------
+  const int qi = q0 + wave * 32 + (lane & 31);
+  const bool qok = qi < N;
+  u32x4 qf[4];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    qrow[t] = (wave * QT + t) * 32 + (lane & 31);
-    const int qi = q0 + qrow[t];
-#pragma unroll
-    for (int kd = 0; kd < 4; ++kd) {
-      qf[t][kd] = (qi < N) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
-                           : u32x4{0, 0, 0, 0};
-    }
+  for (int kd = 0; kd < 4; ++kd) {
+    qf[kd] = qok ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
+                 : u32x4{0, 0, 0, 0};
   }
 
   const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
@@ -95,30 +91,41 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
   constexpr int CH = (kTileKeys * kD / 8) / NT;  // 16-byte chunks of K (and of V) per thread
   static_assert(CH >= 1, "workgroup too large for one tile");
-  int ch_r[CH], ch_c[CH], ch_off[CH], ch_lds[CH];
+  int ch_r[CH], ch_c[CH], ch_voff[CH], ch_lds[CH];
 #pragma unroll
   for (int s = 0; s < CH; ++s) {
     const int cid = tid + s * NT;
     const int o = cid >> 3, dc = cid & 7;
     ch_r[s] = o >> 4;
     ch_c[s] = o & 15;
-    ch_off[s] = (o >> 4) * W + (o & 15);
+    ch_voff[s] = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * dc;  // bytes from the tile origin
     ch_lds[s] = o * kKStride + 8 * dc;
   }
-  const int dcol = 8 * (tid & 7);
   u32x4 kreg[CH], vreg[CH];
   const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head * kD, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head * kD, head_bytes);
 
   auto load_tile = [&](TilePos p) {
-    const int base = p.kh * W + p.kw;
+    if constexpr (ALIGNED) {
+      // Every cell of a tile lies in the grid; the tile origin goes in the
+      // scalar offset.  Past the last tile (kw >= W) tile 0 is re-read: the
+      // slot it is stored to is never read again.
+      const int org = (p.kw < W ? p.kh * W + p.kw : 0) * (kD * 2);
 #pragma unroll
-    for (int s = 0; s < CH; ++s) {
-      const bool ok = (p.kh + ch_r[s] < H) && (p.kw + ch_c[s] < W);
-      const int off = ok ? ((base + ch_off[s]) * kD + dcol) * 2 : kOob;
-      kreg[s] = buf_load16(krs, off);
-      vreg[s] = buf_load16(vrs, off);
+      for (int s = 0; s < CH; ++s) {
+        kreg[s] = buf_load16(krs, ch_voff[s], org);
+        vreg[s] = buf_load16(vrs, ch_voff[s], org);
+      }
+    } else {
+      const int org = (p.kh * W + p.kw) * (kD * 2);
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        const bool ok = (p.kh + ch_r[s] < H) && (p.kw + ch_c[s] < W);
+        const int off = ok ? org + ch_voff[s] : kOob;
+        kreg[s] = buf_load16(krs, off);
+        vreg[s] = buf_load16(vrs, off);
+      }
     }
   };
   auto store_tile = [&](int slot) {
@@ -136,52 +143,58 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
     }
   };
 
-  // ---- bias: rel_w' (x log2 e) for the lane's 8 key columns of a band and
-  // rel_h' for the 4 grid rows of a tile; -inf outside the grid.
+  // ---- bias ------------------------------------------------------------------
+  // rel_w enters through the Q.K^T MFMA: the first MFMA of each 32-key half
+  // accumulates onto rwc, which holds rel_w * log2(e) / c2 for the key column
+  // of each accumulator register (the same 8 columns repeat in both halves and
+  // in both grid rows of a half), so after the multiply by c2 below the score
+  // already carries its rel_w term.  rel_h (4 grid rows per tile) is
+  // prefetched one tile ahead and added with the running maximum in one fma.
   const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
   const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
-  int rw_off[QT], rh_off[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int qi = q0 + qrow[t];
-    rw_off[t] = (qi < N ? qi : 0) * W * 4;
-    rh_off[t] = (qi < N ? qi : 0) * H * 4;
-  }
-  float rw[QT][8];
+  const int qrow = qok ? qi : 0;
+  const int rw_lane = (qrow * W + 4 * half) * 4;  // bytes: this lane's row, column 4*half
+  const int rh_lane = qrow * H * 4;
+  f32x16 rwc;
   auto load_band = [&](int kw0) {
+    float x[8];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const float x = buf_loadf(rwrs, c < W ? rw_off[qt] + 4 * c : kOob);
-        rw[qt][i] = (c < W) ? x * kLog2e : -__builtin_inff();
+    for (int i = 0; i < 8; ++i) {
+      const int dc = 8 * (i >> 2) + (i & 3);  // column offset beyond 4*half
+      if constexpr (ALIGNED) {
+        x[i] = buf_loadf(rwrs, rw_lane + 4 * dc, 4 * kw0) * rw_mul;
+      } else {
+        const int c = kw0 + dc + 4 * half;
+        const float y = buf_loadf(rwrs, c < W ? rw_lane + 4 * (kw0 + dc) : kOob);
+        x[i] = c < W ? y * rw_mul : -__builtin_inff();
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rwc[r] = x[4 * ((r >> 2) & 1) + (r & 3)];
   };
-  float rhn[QT][4];  // rel_h' of the next tile's 4 grid rows
+  float rhn[4];  // rel_h of the next tile's 4 grid rows (-inf outside the grid)
   auto load_rh = [&](int kh0) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = buf_loadf(rhrs, kh0 + r < H ? rh_off[qt] + 4 * (kh0 + r) : kOob);
-        rhn[qt][r] = (kh0 + r < H) ? x * kLog2e : -__builtin_inff();
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (ALIGNED) {
+        rhn[r] = buf_loadf(rhrs, rh_lane + 4 * r, 4 * kh0);
+      } else {
+        const float y = buf_loadf(rhrs, kh0 + r < H ? rh_lane + 4 * (kh0 + r) : kOob);
+        rhn[r] = kh0 + r < H ? y : -__builtin_inff();
       }
+    }
   };
 
   // ---- tile compute pieces -----------------------------------------------
-  // S^T = K Q^T for the tile in `slot` (two 32-key halves per query tile).
-  auto qk = [&](int slot, f32x16 (&s)[QT][2]) {
+  // S^T = K Q^T (+ rel_w term) for the tile in `slot`, two 32-key halves.
+  auto qk = [&](int slot, f32x16 (&s)[2]) {
     const uint16_t* kb = Ks + slot * kTileHalves;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[qt][st] = f32x16{};
-#pragma unroll
       for (int kd = 0; kd < 4; ++kd) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32<BF16>(kf, qf[qt][kd], s[qt][st]);
+        s[st] = mfma32<BF16>(kf, qf[kd], kd == 0 ? rwc : s[st]);
       }
     }
   };
@@ -189,9 +202,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   const int grp = lane >> 4, jl = lane & 15;
   const int tr_row = 4 * (grp >> 1) + (jl >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (jl & 3);
-  f32x16 acc[QT][2];
+  f32x16 acc[2];
   // O^T += V^T P^T for the tile in `slot`: four 16-key steps, two 32-row d tiles.
-  auto pv = [&](int slot, const u32x4 (&pf)[QT][4]) {
+  auto pv = [&](int slot, const u32x4 (&pf)[4]) {
     const uint16_t* vb = Vs + slot * kTileHalves;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -201,8 +214,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
         const u32x2 lo = ds_read_tr16(vp);
         const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf, pf[qt][ks], acc[qt][dt]);
+        acc[dt] = mfma32<false>(vf, pf[ks], acc[dt]);
       }
     }
   };
@@ -211,31 +223,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   const TilePos p0{0, 0};
   const TilePos p1 = next_tile(p0, H);
   const TilePos p2 = next_tile(p1, H);
+  load_band(0);
   load_tile(p0);
   store_tile(0);
   if (T > 1) {
     load_tile(p1);
     store_tile(1);
   }
-  if (T > 2) load_tile(p2);
+  load_tile(p2);  // outside the grid (never used) when there are fewer than three tiles
   load_rh(0);
   __syncthreads();
 
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    acc[t][0] = f32x16{};
-    acc[t][1] = f32x16{};
-  }
-  float m[QT], l[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    m[t] = 0.f;
-    l[t] = 0.f;
-  }
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+  float m = 0.f, l = 0.f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  f32x16 sA[QT][2], sB[QT][2];
-  u32x4 pA[QT][4], pB[QT][4];
+  f32x16 sA[2], sB[2];
+  u32x4 pA[4], pB[4];
   qk(0, sA);
 
   TilePos pc = p0;                // tile t
@@ -245,12 +250,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   // tile t (sc -> pcur) and P.V of tile t-1 (pprev), all in one basic block so
   // the MFMA and VALU streams interleave; then the rare maximum move, the
   // staging of tile t+2 and one barrier.
-  auto step = [&](int t, auto first_c, auto last_c, f32x16 (&sc)[QT][2], f32x16 (&sn)[QT][2],
-                  u32x4 (&pprev)[QT][4], u32x4 (&pcur)[QT][4]) {
+  auto step = [&](int t, auto first_c, auto last_c, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  u32x4 (&pprev)[4], u32x4 (&pcur)[4]) {
     constexpr bool kFirst = decltype(first_c)::value;
     constexpr bool kLast = decltype(last_c)::value;
-    if (pc.kh == 0) load_band(pc.kw);
     const TilePos pn = next_tile(pc, H);
+    if constexpr (!kLast) {
+      if (pn.kh == 0) load_band(pn.kw);  // tile t+1 opens a new column band
+    }
 
     // Operands of this step's MFMAs: K^T fragments of tile t+1 and V^T
     // fragments of tile t-1, read from LDS two chunks ahead of their use.
@@ -276,11 +283,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // Eight chunks, each: one Q.K^T MFMA of tile t+1, one P.V MFMA of tile
-    // t-1 and the softmax of four of tile t's scores per query tile.  The
-    // fences keep this order so the matrix cores run under the VALU work.
-    float tsum[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) tsum[qt] = 0.f;
+    // t-1 and the softmax of four of tile t's scores.  The fences keep this
+    // order so the matrix cores run under the VALU work.
+    float tsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 2 < 8) {
@@ -289,47 +294,40 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
       }
       if constexpr (!kLast) {
         const int st = i & 1, kd = i >> 1;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          sn[qt][st] = mfma32<BF16>(kf[i], qf[qt][kd], kd == 0 ? f32x16{} : sn[qt][st]);
-        }
+        sn[st] = mfma32<BF16>(kf[i], qf[kd], kd == 0 ? rwc : sn[st]);
       }
       if constexpr (!kFirst) {
         const int dt = i & 1, ks = i >> 1;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32<false>(vf[i], pprev[qt][ks], acc[qt][dt]);
+        acc[dt] = mfma32<false>(vf[i], pprev[ks], acc[dt]);
       }
-      // scores 4*i .. 4*i+3 of the lane: st = i/4, g = i%4
+      // scores 4*i .. 4*i+3 of the lane: st = i/4, g = i%4, grid row 2*st + g/2
       const int st = i >> 2, g = i & 3;
+      const float rhm = __builtin_fmaf(rhn[2 * st + (g >> 1)], kLog2e, -m);
+      float x[4];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float rhm = rhn[qt][2 * st + (g >> 1)] - m[qt];
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float b = rw[qt][4 * (g & 1) + e] + rhm;
-          x[e] = __builtin_fmaf(sc[qt][st][4 * g + e], c2, b);
-          sc[qt][st][4 * g + e] = x[e];
-        }
-        const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
-        const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
-        tsum[qt] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum[qt], false);
-        tsum[qt] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum[qt], false);
-        // registers 8*gg + 2*j of S tile st map to P operand (2*st + gg), word j
-        pcur[qt][2 * st + (g >> 1)][2 * (g & 1)] = w0;
-        pcur[qt][2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
+      for (int e = 0; e < 4; ++e) {
+        x[e] = __builtin_fmaf(sc[st][4 * g + e], c2, rhm);
+        sc[st][4 * g + e] = x[e];
       }
+      const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
+      const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum, false);
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum, false);
+      // registers 8*gg + 2*j of S half st map to P operand (2*st + gg), word j
+      pcur[2 * st + (g >> 1)][2 * (g & 1)] = w0;
+      pcur[2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
       if ((i + 1) % kChunksPerFence == 0) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!kLast) load_rh(pn.kh);  // rel_h' of tile t+1 (this tile's values are used)
+    if constexpr (!kLast) load_rh(pn.kh);  // rel_h of tile t+1 (this tile's values are used)
 
     // tile t+2: registers -> LDS slot (t+2)%4 (last read in iteration t-1);
-    // then start the global loads of tile t+3.
-    if (t + 2 < T) store_tile((t + 2) & (kSlots - 1));
-    if (t + 3 < T) load_tile(pl);
-    bool grow = kFirst;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) grow = grow || !(tsum[qt] <= kGrowLimit);
+    // then start the global loads of tile t+3.  Both run unconditionally so the
+    // step stays one basic block (a branch here lets the compiler sink the
+    // softmax below it, away from the MFMAs): past the last tile the slot
+    // written is never read again.
+    store_tile((t + 2) & (kSlots - 1));
+    load_tile(pl);
+    const bool grow = kFirst || !(tsum <= kGrowLimit);
 
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       // Move the reference maximum: exact tile maximum per query, then
@@ -337,45 +335,41 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
       // tile's p against the new m.  (The empty volatile asm keeps this rare
       // block a real branch instead of code speculated on every tile.)
       __asm__ volatile("; reference maximum moves" ::);
+      float mx = -__builtin_inff();
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float mx = -__builtin_inff();
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[qt][st][r]);
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        float inc;
-        if (kFirst) {
-          inc = mx;  // O and l are still zero: only set m
-        } else {
-          inc = __builtin_fmaxf(mx, 0.f);
-          const float alpha = exp2_fast(-inc);
-          l[qt] *= alpha;
-          acc[qt][0] *= alpha;
-          acc[qt][1] *= alpha;
-        }
-        m[qt] += inc;
-        float ts = 0.f;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              w4[i] = pack_f16(exp2_fast(sc[qt][st][8 * gg + 2 * i] - inc),
-                               exp2_fast(sc[qt][st][8 * gg + 2 * i + 1] - inc));
-              ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
-            }
-            pcur[qt][2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-          }
-        }
-        tsum[qt] = ts;
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[st][r]);
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      float inc;
+      if (kFirst) {
+        inc = mx;  // O and l are still zero: only set m
+      } else {
+        inc = __builtin_fmaxf(mx, 0.f);
+        const float alpha = exp2_fast(-inc);
+        l *= alpha;
+        acc[0] *= alpha;
+        acc[1] *= alpha;
       }
-    }
+      m += inc;
+      float ts = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) l[qt] += tsum[qt];
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            w4[i] = pack_f16(exp2_fast(sc[st][8 * gg + 2 * i] - inc),
+                             exp2_fast(sc[st][8 * gg + 2 * i + 1] - inc));
+            ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
+          }
+          pcur[2 * st + gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+      }
+      tsum = ts;
+    }
+    l += tsum;
 
     __syncthreads();
     pl = next_tile(pl, H);
@@ -406,53 +400,58 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
+  const float lt = l + __shfl_xor(l, 32);
+  if (!qok) return;
+  const float inv = 1.0f / lt;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32);
-    const int qi = q0 + qrow[qt];
-    if (qi >= N) continue;
-    const float inv = 1.0f / lt;
+  for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * half;
-        const f32x4 o4 = {acc[qt][dt][4 * g] * inv, acc[qt][dt][4 * g + 1] * inv,
-                          acc[qt][dt][4 * g + 2] * inv, acc[qt][dt][4 * g + 3] * inv};
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
-        } else {
-          const u32x2 pk = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
-                                : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (head + qi) * kD + d) = pk;
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * half;
+      const f32x4 o4 = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
+                        acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
+      } else {
+        const u32x2 pk = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
+                              : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (head + qi) * kD + d) = pk;
       }
     }
   }
 }
 
-template <bool BF16, bool OUT_F32, int NW, int QT>
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED>
 hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
-  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, QT>;
+  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
-  constexpr int BM = 32 * NW * QT;
+  constexpr int BM = 32 * NW;
   const int q_tiles = (a.H * a.W + BM - 1) / BM;
   dim3 grid(static_cast<unsigned>(q_tiles * a.BH));
+  const float c2 = a.scale * kLog2e;
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, q_tiles, a.scale * kLog2e);
+                     a.H, a.W, q_tiles, c2, kLog2e / c2);
   return hipGetLastError();
+}
+
+template <bool BF16, bool OUT_F32, int NW>
+hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
+  // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
+  const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
+  return aligned ? launch_cfg<BF16, OUT_F32, NW, true>(a, lds, stream)
+                 : launch_cfg<BF16, OUT_F32, NW, false>(a, lds, stream);
 }
 
 template <bool BF16, bool OUT_F32>
 hipError_t launch_dt(const AttnArgs& a, int nw, size_t lds, hipStream_t stream) {
   switch (nw) {
-    case 4: return launch_cfg<BF16, OUT_F32, 4, 1>(a, lds, stream);
-    case 2: return launch_cfg<BF16, OUT_F32, 2, 1>(a, lds, stream);
-    default: return launch_cfg<BF16, OUT_F32, 1, 1>(a, lds, stream);
+    case 4: return launch_nw<BF16, OUT_F32, 4>(a, lds, stream);
+    case 2: return launch_nw<BF16, OUT_F32, 2>(a, lds, stream);
+    default: return launch_nw<BF16, OUT_F32, 1>(a, lds, stream);
   }
 }
 
