@@ -4,8 +4,8 @@
 // block, no dense [N, N] bias).
 //
 // Work layout
-//   * A workgroup owns BM = 32*QT*NW consecutive queries of one (batch, head);
-//     each of its NW waves owns 32*QT of them (QT query tiles of 32).
+//   * A workgroup owns BM = 32*NW consecutive queries of one (batch, head);
+//     each of its NW waves owns 32 of them.
 //   * Keys are visited in 2-D tiles of the key grid: 4 grid rows x 16 grid
 //     columns = 64 keys, in column bands (kw0 outer, kh0 inner).  Key o
 //     (0..63) of a tile is grid cell (kh0 + o/16, kw0 + o%16); cells outside
@@ -53,7 +53,7 @@ namespace {
 using namespace attn;
 
 template <bool BF16, bool OUT_F32, int NW, bool ALIGNED>
-__global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
@@ -449,9 +449,9 @@ hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
 template <bool BF16, bool OUT_F32>
 hipError_t launch_dt(const AttnArgs& a, int nw, size_t lds, hipStream_t stream) {
   switch (nw) {
+    case 8: return launch_nw<BF16, OUT_F32, 8>(a, lds, stream);
     case 4: return launch_nw<BF16, OUT_F32, 4>(a, lds, stream);
-    case 2: return launch_nw<BF16, OUT_F32, 2>(a, lds, stream);
-    default: return launch_nw<BF16, OUT_F32, 1>(a, lds, stream);
+    default: return launch_nw<BF16, OUT_F32, 2>(a, lds, stream);
   }
 }
 
@@ -469,7 +469,7 @@ size_t attn_lds_bytes(int cfg, int H, int W) {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
   if (cfg >= 3) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
-  const int nw = cfg == 0 ? 4 : (cfg == 1 ? 2 : 1);
+  const int nw = cfg == 0 ? 8 : (cfg == 1 ? 4 : 2);
   const size_t lds = attn32_lds_bytes();
   if (a.bf16) {
     return a.out_f32 ? launch_dt<true, true>(a, nw, lds, stream) : launch_dt<true, false>(a, nw, lds, stream);

@@ -35,7 +35,7 @@ struct AttnArgs {
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
 // Attention launch configurations:
-//   0, 1, 2: 32 queries per wave, 4, 2 or 1 waves per workgroup (default: 0)
+//   0, 1, 2: 32 queries per wave, 8, 4 or 2 waves per workgroup (default: 0)
 //   3: 16 queries per wave, 4 waves per workgroup (64 queries)
 //   4: 16 queries per wave, 8 waves per workgroup (128 queries)
 int attn_num_configs();
