@@ -226,11 +226,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   load_band(0);
   load_tile(p0);
   store_tile(0);
-  if (T > 1) {
-    load_tile(p1);
-    store_tile(1);
-  }
-  load_tile(p2);  // outside the grid (never used) when there are fewer than three tiles
+  load_tile(p1);  // tiles past the last one are staged too (from outside the grid) and never used
+  store_tile(1);
+  load_tile(p2);
   load_rh(0);
   __syncthreads();
 
@@ -249,15 +247,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   // One pipeline step for tile t: Q.K^T of tile t+1 (into sn), softmax of
   // tile t (sc -> pcur) and P.V of tile t-1 (pprev), all in one basic block so
   // the MFMA and VALU streams interleave; then the rare maximum move, the
-  // staging of tile t+2 and one barrier.
-  auto step = [&](int t, auto first_c, auto last_c, f32x16 (&sc)[2], f32x16 (&sn)[2],
+  // staging of tile t+2 and one barrier.  The last step also multiplies the
+  // slot after the last tile (data staged from outside the grid) and drops
+  // the result: one code path for every step keeps register pressure low.
+  auto step = [&](int t, auto first_c, f32x16 (&sc)[2], f32x16 (&sn)[2],
                   u32x4 (&pprev)[4], u32x4 (&pcur)[4]) {
     constexpr bool kFirst = decltype(first_c)::value;
-    constexpr bool kLast = decltype(last_c)::value;
     const TilePos pn = next_tile(pc, H);
-    if constexpr (!kLast) {
-      if (pn.kh == 0) load_band(pn.kw);  // tile t+1 opens a new column band
-    }
+    if (pn.kh == 0 && pn.kw < W) load_band(pn.kw);  // tile t+1 opens a new column band
 
     // Operands of this step's MFMAs: K^T fragments of tile t+1 and V^T
     // fragments of tile t-1, read from LDS two chunks ahead of their use.
@@ -277,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     u32x4 kf[8], vf[8];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (!kLast) kf[i] = read_k(i);
+      kf[i] = read_k(i);
       if constexpr (!kFirst) vf[i] = read_v(i);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -289,10 +286,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 2 < 8) {
-        if constexpr (!kLast) kf[i + 2] = read_k(i + 2);
+        kf[i + 2] = read_k(i + 2);
         if constexpr (!kFirst) vf[i + 2] = read_v(i + 2);
       }
-      if constexpr (!kLast) {
+      {
         const int st = i & 1, kd = i >> 1;
         sn[st] = mfma32<BF16>(kf[i], qf[kd], kd == 0 ? rwc : sn[st]);
       }
@@ -318,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
       pcur[2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
       if ((i + 1) % kChunksPerFence == 0) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!kLast) load_rh(pn.kh);  // rel_h of tile t+1 (this tile's values are used)
+    load_rh(pn.kh);  // rel_h of tile t+1 (this tile's values are used); row 0 past the grid
 
     // tile t+2: registers -> LDS slot (t+2)%4 (last read in iteration t-1);
     // then start the global loads of tile t+3.  Both run unconditionally so the
@@ -379,24 +376,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
   const int slot_last = (T - 1) & (kSlots - 1);
-  if (T == 1) {
-    step(0, True{}, True{}, sA, sB, pB, pA);
-    pv(slot_last, pA);
+  step(0, True{}, sA, sB, pB, pA);
+  int t = 1;
+  for (; t + 1 < T; t += 2) {
+    step(t, False{}, sB, sA, pA, pB);
+    step(t + 1, False{}, sA, sB, pB, pA);
+  }
+  if (t < T) {  // an even number of tiles: one step left
+    step(t, False{}, sB, sA, pA, pB);
+    pv(slot_last, pB);
   } else {
-    step(0, True{}, False{}, sA, sB, pB, pA);
-    int t = 1;
-    for (; t + 2 < T; t += 2) {
-      step(t, False{}, False{}, sB, sA, pA, pB);
-      step(t + 1, False{}, False{}, sA, sB, pB, pA);
-    }
-    if (t + 2 == T) {
-      step(t, False{}, False{}, sB, sA, pA, pB);
-      step(t + 1, False{}, True{}, sA, sB, pB, pA);
-      pv(slot_last, pA);
-    } else {
-      step(t, False{}, True{}, sB, sA, pA, pB);
-      pv(slot_last, pB);
-    }
+    pv(slot_last, pA);
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
