@@ -122,6 +122,30 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
                               float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
                               void* stream);
 
+/*
+ * relpos_attn_config: the launch configuration relpos_attn_fwd uses for a
+ * problem on a device with `cu_count` compute units.  Host-only: it launches
+ * nothing and touches no device, so it can be called anywhere.
+ *
+ *   0: workgroups of 8 waves x 32 queries, one workgroup per compute unit;
+ *      a workgroup's two waves per SIMD share one K/V staging.
+ *   1: workgroups of 4 waves x 32 queries, two per compute unit.
+ *
+ * The choice compares the time, in workgroup rounds, that each needs for the
+ * B*heads*ceil(H*W / (32*waves)) workgroups: configuration 0 counts every
+ * started round as a full one (at 0.95 of a configuration-1 round for bf16
+ * inputs, whose V conversion it shares, 1.0 for fp16); configuration 1
+ * counts a last round with at most one workgroup per compute unit at 0.77
+ * (a lone workgroup runs one wave per SIMD, measured faster per tile).
+ * Ties go to 0.  Inside relpos_attn_fwd the environment variable
+ * RELPOS_ATTN_CFG=<0..4> overrides the choice (configurations 2..4 are
+ * slower alternatives kept for comparison).
+ * Returns -1 if a size or the dtype is out of range (as relpos_attn_fwd
+ * checks them) or cu_count < 1.
+ */
+int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
+                       int cu_count);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* relpos_status_string(relpos_status s);
 

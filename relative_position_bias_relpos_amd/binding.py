@@ -50,6 +50,8 @@ def _load():
         lib.relpos_status_string.argtypes = [i32]
         lib.relpos_abi_version.restype = i32
         lib.relpos_abi_version.argtypes = []
+        lib.relpos_attn_config.restype = i32
+        lib.relpos_attn_config.argtypes = [i64, i64, i64, i64, i32, i32]
         _lib = lib
         return lib
 
@@ -60,6 +62,15 @@ def status_string(status):
 
 def abi_version():
     return _load().relpos_abi_version()
+
+
+def attn_config(B, heads, H, W, dtype, cu_count):
+    """Launch configuration relpos_attn_fwd uses for this problem on a device
+    with `cu_count` compute units (0: 8-wave workgroups, 1: 4-wave); host-only."""
+    c = _load().relpos_attn_config(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count))
+    if c < 0:
+        raise ValueError("sizes or dtype out of range for relpos_attn_fwd")
+    return c
 
 
 def _ptr(t):

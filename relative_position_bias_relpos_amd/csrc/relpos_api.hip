@@ -78,10 +78,14 @@ relpos_status check_device(const Operand* ops, int n) {
   return RELPOS_OK;
 }
 
-// Per-device cache of the LDS a workgroup may use.
-int device_lds_limit(int* out) {
+// Per-device cache of the LDS a workgroup may use and the compute-unit count.
+struct DeviceProps {
+  int lds_limit;
+  int cus;
+};
+int device_props(DeviceProps* out) {
   static std::once_flag once[kMaxDevices];
-  static int limit[kMaxDevices];
+  static DeviceProps props[kMaxDevices];
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -93,14 +97,20 @@ int device_lds_limit(int* out) {
       (void)hipGetLastError();
       v = 65536;
     }
-    limit[dev] = v;
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) {
+      (void)hipGetLastError();
+      c = 256;
+    }
+    props[dev] = DeviceProps{v, c};
   });
-  *out = limit[dev];
+  *out = props[dev];
   return 0;
 }
 
-// Order in which attention configurations are tried (first that fits LDS).
-constexpr int kAttnPreference[] = {0, 1, 2, 3, 4};
+// Order in which attention configurations are tried when the chosen one does
+// not fit the device's LDS.
+constexpr int kAttnFallback[] = {0, 1, 2, 3, 4};
 
 // Tuning knob: RELPOS_ATTN_CFG=<0..4> forces one configuration when it fits
 // (read on every call, so one process can compare configurations).
@@ -116,6 +126,13 @@ int forced_attn_config() {
 extern "C" {
 
 int relpos_abi_version(void) { return RELPOS_ABI_VERSION; }
+
+int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
+                       int cu_count) {
+  int64_t BH = 0;
+  if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
+  return relpos::attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, cu_count);
+}
 
 const char* relpos_status_string(relpos_status s) {
   switch (s) {
@@ -192,18 +209,21 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
   }
   if ((st = check_device(ops, 6)) != RELPOS_OK) return st;
 
-  int lds_limit = 0;
-  if (device_lds_limit(&lds_limit) != 0) return RELPOS_E_HIP;
-  int cfg = -1;
-  const int forced = forced_attn_config();
-  if (forced >= 0 && relpos::attn_lds_bytes(forced, static_cast<int>(H), static_cast<int>(W)) <=
-                         static_cast<size_t>(lds_limit)) {
-    cfg = forced;
-  }
-  for (int cand : kAttnPreference) {
-    if (cfg >= 0) break;
-    if (relpos::attn_lds_bytes(cand, static_cast<int>(H), static_cast<int>(W)) <= static_cast<size_t>(lds_limit)) {
-      cfg = cand;
+  DeviceProps props{};
+  if (device_props(&props) != 0) return RELPOS_E_HIP;
+  auto fits = [&](int c) {
+    return relpos::attn_lds_bytes(c, static_cast<int>(H), static_cast<int>(W)) <=
+           static_cast<size_t>(props.lds_limit);
+  };
+  int cfg = forced_attn_config();
+  if (cfg < 0 || !fits(cfg)) cfg = relpos::attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, props.cus);
+  if (!fits(cfg)) {
+    cfg = -1;
+    for (int cand : kAttnFallback) {
+      if (fits(cand)) {
+        cfg = cand;
+        break;
+      }
     }
   }
   if (cfg < 0) return RELPOS_E_SHAPE;

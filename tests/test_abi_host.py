@@ -141,3 +141,47 @@ def test_aliasing(lib):
     p = list(P[:5])
     p[3] = p[0]  # rel_h over q
     assert build(lib, ptrs=p) == E_ALIAS
+
+
+# ---- launch configuration choice (host-only cost model) ----------------------
+
+def _cfg(lib, B, heads, H, W, dt, cus=256):
+    lib.relpos_attn_config.restype = ctypes.c_int
+    lib.relpos_attn_config.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
+    return lib.relpos_attn_config(B, heads, H, W, dt, cus)
+
+
+def test_attn_config_on_the_workloads(lib):
+    # 64x64, 12 heads: 192 workgroups of 8 waves fit in one round; 384 of 4
+    # waves leave half the CUs with two workgroups -> 8 waves.
+    assert _cfg(lib, 1, 12, 64, 64, BF16) == 0
+    # 48x80, 2x12 heads: 360 workgroups of 8 waves need two full rounds; 720
+    # of 4 waves end with 208 lone workgroups -> 4 waves.
+    assert _cfg(lib, 2, 12, 48, 80, BF16) == 1
+    # 96x96, 2x16 heads: 5 rounds x 0.95 = 4.75 against 4 + 0.77.
+    assert _cfg(lib, 2, 16, 96, 96, BF16) == 0
+    # fp16 64x64, 4x12 heads: 3 rounds each, the tie goes to 8 waves.
+    assert _cfg(lib, 4, 12, 64, 64, FP16) == 0
+
+
+def test_attn_config_rounds_arithmetic(lib):
+    # One (b, h) of 64 queries: one 8-wave round (0.95) against one lone
+    # 4-wave workgroup (0.77).
+    assert _cfg(lib, 1, 1, 8, 8, BF16) == 1
+    # 512 heads of 256 queries: exactly two full 4-wave rounds (1024
+    # workgroups) against two 8-wave rounds at 0.95 (bf16) or 1.0 (fp16; the
+    # tie goes to 0).
+    assert _cfg(lib, 1, 512, 16, 16, BF16) == 0
+    assert _cfg(lib, 1, 512, 16, 16, FP16) == 0
+    # 1024 heads of 128 queries: an 8-wave workgroup would be half empty
+    # (four rounds) against two full 4-wave rounds.
+    assert _cfg(lib, 1, 1024, 16, 8, BF16) == 1
+    # The CU count enters: on 128 CUs the 64x64 workload needs two 8-wave
+    # rounds (1.9) against 384 = 1.5 rounds of 4 waves (1 + 0.77).
+    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128) == 1
+
+
+def test_attn_config_rejects_bad_input(lib):
+    assert _cfg(lib, 1, 1, 0, 8, BF16) == -1
+    assert _cfg(lib, 1, 1, 8, 8, FP32) == -1
+    assert _cfg(lib, 1, 1, 8, 8, BF16, cus=0) == -1
