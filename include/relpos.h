@@ -134,10 +134,10 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
  * The choice compares the time, in workgroup rounds, that each needs for the
  * B*heads*ceil(H*W / (32*waves)) workgroups: configuration 0 counts every
  * started round as a full one (at 0.95 of a configuration-1 round for bf16
- * inputs, whose V conversion it shares, 1.0 for fp16); configuration 1
- * counts a last round with at most one workgroup per compute unit at 0.77
- * (a lone workgroup runs one wave per SIMD, measured faster per tile).
- * Ties go to 0.  Inside relpos_attn_fwd the environment variable
+ * inputs, whose V conversion it shares, and 1.03 for fp16, which needs none;
+ * both measured); configuration 1 counts a last round with at most one
+ * workgroup per compute unit at 0.77 (a lone workgroup runs one wave per
+ * SIMD, measured faster per tile).  Ties go to 0.  Inside relpos_attn_fwd the environment variable
  * RELPOS_ATTN_CFG=<0..4> overrides the choice (configurations 2..4 are
  * slower alternatives kept for comparison).
  * Returns -1 if a size or the dtype is out of range (as relpos_attn_fwd

@@ -108,6 +108,21 @@ int device_props(DeviceProps* out) {
   return 0;
 }
 
+// Attention configuration 0 (8-wave workgroups) or 1 (4-wave) for B*heads =
+// BH problems of N queries on `cus` compute units; the cost model is the one
+// documented with relpos_attn_config in include/relpos.h.
+int attn_auto_config(int64_t BH, int64_t N, bool bf16, int cus) {
+  // Configuration 0 (one workgroup per CU): every started round is a full
+  // round.  Configuration 1 (two per CU): a last round with at most one
+  // workgroup per CU runs those workgroups alone on their CUs.
+  const int64_t g8 = BH * ((N + 255) / 256);
+  const int64_t g4 = BH * ((N + 127) / 128);
+  const double t8 = (bf16 ? 0.95 : 1.03) * static_cast<double>((g8 + cus - 1) / cus);
+  const int64_t full = g4 / (2 * cus), rem = g4 % (2 * cus);
+  const double t4 = static_cast<double>(full) + (rem == 0 ? 0.0 : (rem <= cus ? 0.77 : 1.0));
+  return t8 <= t4 ? 0 : 1;
+}
+
 // Order in which attention configurations are tried when the chosen one does
 // not fit the device's LDS.
 constexpr int kAttnFallback[] = {0, 1, 2, 3, 4};
@@ -131,7 +146,7 @@ int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dt
                        int cu_count) {
   int64_t BH = 0;
   if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
-  return relpos::attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, cu_count);
+  return attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, cu_count);
 }
 
 const char* relpos_status_string(relpos_status s) {
@@ -216,7 +231,7 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
            static_cast<size_t>(props.lds_limit);
   };
   int cfg = forced_attn_config();
-  if (cfg < 0 || !fits(cfg)) cfg = relpos::attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, props.cus);
+  if (cfg < 0 || !fits(cfg)) cfg = attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, props.cus);
   if (!fits(cfg)) {
     cfg = -1;
     for (int cand : kAttnFallback) {

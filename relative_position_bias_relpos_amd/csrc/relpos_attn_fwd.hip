@@ -451,18 +451,6 @@ size_t attn32_lds_bytes() { return 2 * kSlots * static_cast<size_t>(kTileHalves)
 
 int attn_num_configs() { return 5; }
 
-int attn_auto_config(int64_t BH, int64_t N, bool bf16, int cus) {
-  // Configuration 0 (8 waves, one workgroup per CU): every started round is
-  // a full round.  Configuration 1 (4 waves, two per CU): a last round with
-  // at most one workgroup per CU runs those workgroups alone on their CUs.
-  const int64_t g8 = BH * ((N + 255) / 256);
-  const int64_t g4 = BH * ((N + 127) / 128);
-  const double t8 = (bf16 ? 0.95 : 1.0) * static_cast<double>((g8 + cus - 1) / cus);
-  const int64_t full = g4 / (2 * cus), rem = g4 % (2 * cus);
-  const double t4 = static_cast<double>(full) + (rem == 0 ? 0.0 : (rem <= cus ? 0.77 : 1.0));
-  return t8 <= t4 ? 0 : 1;
-}
-
 size_t attn_lds_bytes(int cfg, int H, int W) {
   (void)H;
   (void)W;

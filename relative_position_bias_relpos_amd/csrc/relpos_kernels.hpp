@@ -39,9 +39,6 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 //   3: 16 queries per wave, 4 waves per workgroup (64 queries)
 //   4: 16 queries per wave, 8 waves per workgroup (128 queries)
 int attn_num_configs();
-// Configuration 0 or 1 for B*heads = BH problems of N queries on `cus` CUs
-// (the cost model documented with relpos_attn_config).
-int attn_auto_config(int64_t BH, int64_t N, bool bf16, int cus);
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
