@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 1
+#define RELPOS_ABI_VERSION 2
 
 typedef enum relpos_dtype {
   RELPOS_BF16 = 0,
@@ -108,7 +108,8 @@ relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel
  *   rel_w      [B, heads, H*W, W]   fp32
  *   out        [B, heads, H*W, D]   out_dtype, written; must not overlap any input
  *   B, heads   >= 0, B*heads <= 65535 (B*heads == 0 is an OK no-op)
- *   H, W       >= 1, H*W <= 2^24, H <= 4096, W <= 4096
+ *   H, W       >= 1, H*W <= 2^24, H <= 4096, W <= 4096, and
+ *              B*heads*ceil(H*W/64) < 2^31
  *   D          must be 64
  *   scale      finite (else E_VALUE); multiplies q.k only (not the bias)
  *   in_dtype   RELPOS_BF16 or RELPOS_FP16
@@ -123,28 +124,84 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
                               void* stream);
 
 /*
- * relpos_attn_config: the launch configuration relpos_attn_fwd uses for a
- * problem on a device with `cu_count` compute units.  Host-only: it launches
- * nothing and touches no device, so it can be called anywhere.
+ * relpos_attn_fwd_ws: relpos_attn_fwd with a caller-provided workspace, which
+ * lets the launch split the key range of query units across workgroups.
+ *
+ * Same operation, arguments, result tolerance and errors as relpos_attn_fwd,
+ * plus:
+ *   workspace        device memory, 16-byte aligned, not overlapping any
+ *                    other operand.  Scratch: its contents on entry are not
+ *                    read, and on return it holds partial results.  Calls
+ *                    that use one workspace must not run concurrently (on one
+ *                    stream they never do).
+ *   workspace_bytes  its size; >= relpos_attn_workspace_bytes(...) for the
+ *                    current device, else E_SHAPE when the split is chosen.
+ *                    When that value is 0 the workspace is not used and may
+ *                    be NULL.  A negative size is E_VALUE.
+ * Split launch (chosen by the cost model of relpos_attn_config when it is
+ * faster): a grid of one 8-wave workgroup per compute unit (P of them) over
+ * units of 256 consecutive queries of one (b, h), T key tiles each.  The
+ * first floor(units / P) * P units run whole, one round at a time; the rest
+ * of the last round are cut at key tile s = T*k/(k+1) (k = ceil(rest /
+ * (P - rest))): their heads [0, s) run on `rest` workgroups and their tails
+ * [s, T) on the others, k per workgroup, so every workgroup of the last
+ * round has about s tiles.  Heads and tails store their unnormalised
+ * output, reference maximum and row sum in the workspace, and a second
+ * kernel on the same stream merges each unit's head and tail (in that order)
+ * and writes its output.  Results are bitwise reproducible run to run, and
+ * differ from the unsplit launch by rounding only.
+ * Check order: as relpos_attn_fwd up to overlap, then the configuration is
+ * chosen (a device query); if it splits, the workspace is checked (NULL,
+ * alignment, size, overlap), and finally every pointer, the workspace
+ * included, must be device memory of the current device.
+ */
+relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                 const float* rel_h, const float* rel_w, void* out,
+                                 int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                 float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * relpos_attn_workspace_bytes: bytes of workspace relpos_attn_fwd_ws needs for
+ * this problem on a device with `cu_count` compute units: 0 when the split
+ * launch would not be chosen, -1 if a size or the dtype is out of range or
+ * cu_count < 1.  Host-only.  The size is cu_count * 2 * (256*64 + 2*256) * 4
+ * bytes: two piece slots per workgroup.
+ */
+int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W,
+                                    relpos_dtype in_dtype, int cu_count);
+
+/*
+ * relpos_attn_config: the launch configuration relpos_attn_fwd (with_workspace
+ * = 0) or relpos_attn_fwd_ws (with_workspace != 0) uses for a problem on a
+ * device with `cu_count` compute units.  Host-only: it launches nothing and
+ * touches no device, so it can be called anywhere.
  *
  *   0: workgroups of 8 waves x 32 queries, one workgroup per compute unit;
  *      a workgroup's two waves per SIMD share one K/V staging.
  *   1: workgroups of 4 waves x 32 queries, two per compute unit.
+ *   5: configuration 0 with the key range split over one workgroup per
+ *      compute unit (relpos_attn_fwd_ws only).
  *
- * The choice compares the time, in workgroup rounds, that each needs for the
- * B*heads*ceil(H*W / (32*waves)) workgroups: configuration 0 counts every
- * started round as a full one (at 0.95 of a configuration-1 round for bf16
- * inputs, whose V conversion it shares, and 1.03 for fp16, which needs none;
+ * The choice compares times in workgroup rounds (one round = one 4-wave
+ * workgroup per SIMD pair of every compute unit running all T key tiles of
+ * its queries): configuration 0 counts every started round of its
+ * workgroups as a full one, at 0.95 of a configuration-1 round for bf16
+ * inputs (whose V conversion it shares) and 1.03 for fp16 (which needs none;
  * both measured); configuration 1 counts a last round with at most one
  * workgroup per compute unit at 0.77 (a lone workgroup runs one wave per
- * SIMD, measured faster per tile).  Ties go to 0.  Inside relpos_attn_fwd the environment variable
- * RELPOS_ATTN_CFG=<0..4> overrides the choice (configurations 2..4 are
- * slower alternatives kept for comparison).
+ * SIMD, measured faster per tile); configuration 5 costs the 8-wave factor
+ * times (full rounds + (max(s, k*(T - s)) + 4) / T) in the terms of
+ * relpos_attn_fwd_ws, and is considered only with a workspace, a last round
+ * to split and k <= 4.  Ties go to the lower
+ * number.  Inside the calls the environment variable RELPOS_ATTN_CFG=<0..5>
+ * overrides the choice (2..4 are slower alternatives kept for comparison;
+ * 5 only where a large enough workspace is passed).
  * Returns -1 if a size or the dtype is out of range (as relpos_attn_fwd
  * checks them) or cu_count < 1.
  */
 int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
-                       int cu_count);
+                       int cu_count, int with_workspace);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* relpos_status_string(relpos_status s);

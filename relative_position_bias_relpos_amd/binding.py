@@ -50,8 +50,13 @@ def _load():
         lib.relpos_status_string.argtypes = [i32]
         lib.relpos_abi_version.restype = i32
         lib.relpos_abi_version.argtypes = []
+        lib.relpos_attn_fwd_ws.restype = i32
+        lib.relpos_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32,
+                                           vp, i64, vp]
+        lib.relpos_attn_workspace_bytes.restype = i64
+        lib.relpos_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         lib.relpos_attn_config.restype = i32
-        lib.relpos_attn_config.argtypes = [i64, i64, i64, i64, i32, i32]
+        lib.relpos_attn_config.argtypes = [i64, i64, i64, i64, i32, i32, i32]
         _lib = lib
         return lib
 
@@ -64,13 +69,45 @@ def abi_version():
     return _load().relpos_abi_version()
 
 
-def attn_config(B, heads, H, W, dtype, cu_count):
-    """Launch configuration relpos_attn_fwd uses for this problem on a device
-    with `cu_count` compute units (0: 8-wave workgroups, 1: 4-wave); host-only."""
-    c = _load().relpos_attn_config(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count))
+def attn_config(B, heads, H, W, dtype, cu_count, with_workspace=True):
+    """Launch configuration the attention call uses for this problem on a
+    device with `cu_count` compute units (0: 8-wave workgroups, 1: 4-wave,
+    5: key range split, only with a workspace); host-only."""
+    c = _load().relpos_attn_config(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count),
+                                   1 if with_workspace else 0)
     if c < 0:
         raise ValueError("sizes or dtype out of range for relpos_attn_fwd")
     return c
+
+
+def workspace_bytes(B, heads, H, W, dtype, cu_count):
+    """Bytes of workspace relpos_attn_fwd_ws needs (0: no split, none used)."""
+    n = _load().relpos_attn_workspace_bytes(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count))
+    if n < 0:
+        raise ValueError("sizes or dtype out of range for relpos_attn_fwd")
+    return n
+
+
+_cus = {}
+_workspaces = {}  # (device index, stream handle) -> uint8 scratch tensor
+
+
+def _cu_count(device):
+    if device.index not in _cus:
+        _cus[device.index] = torch.cuda.get_device_properties(device).multi_processor_count
+    return _cus[device.index]
+
+
+def _cached_workspace(device, stream, nbytes):
+    """A scratch workspace of at least `nbytes` for one (device, stream); calls
+    on one stream never overlap, so it is reused as is."""
+    key = (device.index, stream)
+    with _lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+        return ws
 
 
 def _ptr(t):
@@ -127,8 +164,15 @@ def relpos_build(q, rel_pos_h, rel_pos_w, H, W, rel_h=None, rel_w=None):
     return rel_h, rel_w
 
 
-def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torch.float32):
-    """out [B,heads,H*W,D] = softmax(scale*q.k + rel_h[:, j/W] + rel_w[:, j%W]) @ v."""
+def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torch.float32,
+                    workspace="auto"):
+    """out [B,heads,H*W,D] = softmax(scale*q.k + rel_h[:, j/W] + rel_w[:, j%W]) @ v.
+
+    workspace: "auto" (default) calls relpos_attn_fwd_ws with a scratch
+    workspace cached per (device, stream), allocated on the first call that
+    needs one; a tensor is used as the workspace; None calls relpos_attn_fwd
+    (no key-range split).
+    """
     lib = _load()
     B, nh, D = _dims(q, H, W)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -146,7 +190,20 @@ def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torc
     _need(out, "out")
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
-    st = lib.relpos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
-                             B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype], _stream(q))
-    _check("relpos_attn_fwd", st)
+    if workspace is None:
+        st = lib.relpos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                                 B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype], _stream(q))
+        _check("relpos_attn_fwd", st)
+        return out
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        need = workspace_bytes(B, nh, H, W, q.dtype, _cu_count(q.device))
+        workspace = _cached_workspace(q.device, _stream(q).value, need) if need > 0 else None
+    ws_ptr = _ptr(workspace)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.relpos_attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                                B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
+                                ws_ptr, ws_len, _stream(q))
+    _check("relpos_attn_fwd_ws", st)
     return out

@@ -108,32 +108,124 @@ int device_props(DeviceProps* out) {
   return 0;
 }
 
-// Attention configuration 0 (8-wave workgroups) or 1 (4-wave) for B*heads =
-// BH problems of N queries on `cus` compute units; the cost model is the one
-// documented with relpos_attn_config in include/relpos.h.
-int attn_auto_config(int64_t BH, int64_t N, bool bf16, int cus) {
+// Attention configuration for B*heads = BH problems on an H x W grid on `cus`
+// compute units: 0 (8-wave workgroups), 1 (4-wave) or, when a workspace is
+// available, kAttnSplitConfig.  The cost model is the one documented with
+// relpos_attn_config in include/relpos.h; times are in 4-wave rounds.
+constexpr int kMergeTiles = 4;  // cost of the merge launch, in tile steps
+int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool allow_split) {
+  const int64_t N = H * W;
+  const int64_t T = ((H + 3) / 4) * ((W + 15) / 16);  // key tiles per query unit
+  const double a8 = bf16 ? 0.95 : 1.03;
   // Configuration 0 (one workgroup per CU): every started round is a full
   // round.  Configuration 1 (two per CU): a last round with at most one
   // workgroup per CU runs those workgroups alone on their CUs.
   const int64_t g8 = BH * ((N + 255) / 256);
   const int64_t g4 = BH * ((N + 127) / 128);
-  const double t8 = (bf16 ? 0.95 : 1.03) * static_cast<double>((g8 + cus - 1) / cus);
+  const double t8 = a8 * static_cast<double>((g8 + cus - 1) / cus);
   const int64_t full = g4 / (2 * cus), rem = g4 % (2 * cus);
   const double t4 = static_cast<double>(full) + (rem == 0 ? 0.0 : (rem <= cus ? 0.77 : 1.0));
-  return t8 <= t4 ? 0 : 1;
+  int best = t8 <= t4 ? 0 : 1;
+  // Split: the full rounds of 8-wave units, then a last round whose heads
+  // and tails (k per idle CU) take max(s, k*(T - s)) tiles, plus the merge;
+  // considered when at most 4 tails share a CU (a gain of 20% or more of the
+  // last round).
+  if (allow_split) {
+    const relpos::SplitPlan sp = relpos::split_plan(g8, static_cast<int>(T), cus);
+    if (sp.rest > 0 && sp.s < T && sp.k <= 4) {
+      const int64_t last = sp.s > sp.k * (T - sp.s) ? sp.s : sp.k * (T - sp.s);
+      const double ts = a8 * (sp.rounds + static_cast<double>(last + kMergeTiles) / static_cast<double>(T));
+      if (ts < (best == 0 ? t8 : t4)) best = relpos::kAttnSplitConfig;
+    }
+  }
+  return best;
 }
 
 // Order in which attention configurations are tried when the chosen one does
 // not fit the device's LDS.
 constexpr int kAttnFallback[] = {0, 1, 2, 3, 4};
 
-// Tuning knob: RELPOS_ATTN_CFG=<0..4> forces one configuration when it fits
-// (read on every call, so one process can compare configurations).
+// Tuning knob: RELPOS_ATTN_CFG=<0..5> forces one configuration when it fits
+// (read on every call, so one process can compare configurations); 5 only
+// applies where a workspace is passed.
 int forced_attn_config() {
   const char* e = std::getenv("RELPOS_ATTN_CFG");
   if (!e || !*e) return -1;
   const int c = std::atoi(e);
   return (c >= 0 && c < relpos::attn_num_configs()) ? c : -1;
+}
+
+// Shared body of relpos_attn_fwd and relpos_attn_fwd_ws.
+relpos_status attn_fwd_impl(const void* q, const void* k, const void* v,
+                            const float* rel_h, const float* rel_w, void* out,
+                            int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                            float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                            bool with_ws, void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t BH = 0;
+  relpos_status st = check_dims(B, heads, H, W, D, &BH);
+  if (st != RELPOS_OK) return st;
+  if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
+  if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
+  if (!std::isfinite(scale)) return RELPOS_E_VALUE;
+  if (BH == 0) return RELPOS_OK;
+  // Workgroup counts (down to 64 queries each) must fit a 1-D grid.
+  if (BH * ((H * W + 63) / 64) >= (int64_t(1) << 31)) return RELPOS_E_SHAPE;
+
+  const size_t N = static_cast<size_t>(H * W);
+  const size_t in_bytes = BH * N * 64 * 2;
+  const size_t out_bytes = BH * N * 64 * (out_dtype == RELPOS_FP32 ? 4 : 2);
+  Operand ops[7] = {
+      {q, in_bytes}, {k, in_bytes}, {v, in_bytes},
+      {rel_h, BH * N * H * 4}, {rel_w, BH * N * W * 4}, {out, out_bytes}, {nullptr, 0},
+  };
+  if ((st = check_align(ops, 6)) != RELPOS_OK) return st;
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
+  }
+
+  DeviceProps props{};
+  if (device_props(&props) != 0) return RELPOS_E_HIP;
+  auto fits = [&](int c) {
+    return relpos::attn_lds_bytes(c, static_cast<int>(H), static_cast<int>(W)) <=
+           static_cast<size_t>(props.lds_limit);
+  };
+  const bool bf16 = in_dtype == RELPOS_BF16;
+  // The workspace is used (and checked) only when the split is chosen.
+  const size_t need = relpos::attn_split_workspace_bytes(BH, H * W, props.cus);
+  const bool can_split = with_ws && workspace != nullptr && static_cast<uint64_t>(workspace_bytes) >= need;
+  int cfg = forced_attn_config();
+  if (cfg == relpos::kAttnSplitConfig && !can_split) cfg = -1;
+  if (cfg < 0 || !fits(cfg)) cfg = attn_auto_config(BH, H, W, bf16, props.cus, with_ws);
+  if (cfg == relpos::kAttnSplitConfig) {
+    if (workspace == nullptr) return RELPOS_E_NULL;
+    ops[6] = Operand{workspace, need};
+    if ((st = check_align(ops + 6, 1)) != RELPOS_OK) return st;
+    if (static_cast<uint64_t>(workspace_bytes) < need) return RELPOS_E_SHAPE;
+    for (int i = 0; i < 6; ++i) {
+      if (overlaps(ops[6], ops[i])) return RELPOS_E_ALIAS;
+    }
+  }
+  if (!fits(cfg)) {
+    cfg = -1;
+    for (int cand : kAttnFallback) {
+      if (fits(cand)) {
+        cfg = cand;
+        break;
+      }
+    }
+  }
+  if (cfg < 0) return RELPOS_E_SHAPE;
+  if ((st = check_device(ops, cfg == relpos::kAttnSplitConfig ? 7 : 6)) != RELPOS_OK) return st;
+
+  relpos::AttnArgs a{q, k, v, rel_h, rel_w, out,
+                     static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
+                     bf16, out_dtype == RELPOS_FP32};
+  if (cfg == relpos::kAttnSplitConfig) {
+    a.ws = workspace;
+    a.split_ctas = props.cus;
+  }
+  if (relpos::launch_attn_fwd(a, cfg, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  return RELPOS_OK;
 }
 
 }  // namespace
@@ -143,10 +235,10 @@ extern "C" {
 int relpos_abi_version(void) { return RELPOS_ABI_VERSION; }
 
 int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
-                       int cu_count) {
+                       int cu_count, int with_workspace) {
   int64_t BH = 0;
   if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
-  return attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, cu_count);
+  return attn_auto_config(BH, H, W, in_dtype == RELPOS_BF16, cu_count, with_workspace != 0);
 }
 
 const char* relpos_status_string(relpos_status s) {
@@ -203,51 +295,26 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
                               int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
                               float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
                               void* stream) {
+  return attn_fwd_impl(q, k, v, rel_h, rel_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
+                       false, nullptr, 0, stream);
+}
+
+int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
+                                    int cu_count) {
   int64_t BH = 0;
-  relpos_status st = check_dims(B, heads, H, W, D, &BH);
-  if (st != RELPOS_OK) return st;
-  if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
-  if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
-  if (!std::isfinite(scale)) return RELPOS_E_VALUE;
-  if (BH == 0) return RELPOS_OK;
+  if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
+  if (attn_auto_config(BH, H, W, in_dtype == RELPOS_BF16, cu_count, true) != relpos::kAttnSplitConfig) return 0;
+  return static_cast<int64_t>(relpos::attn_split_workspace_bytes(BH, H * W, cu_count));
+}
 
-  const size_t N = static_cast<size_t>(H * W);
-  const size_t in_bytes = BH * N * 64 * 2;
-  const size_t out_bytes = BH * N * 64 * (out_dtype == RELPOS_FP32 ? 4 : 2);
-  const Operand ops[6] = {
-      {q, in_bytes}, {k, in_bytes}, {v, in_bytes},
-      {rel_h, BH * N * H * 4}, {rel_w, BH * N * W * 4}, {out, out_bytes},
-  };
-  if ((st = check_align(ops, 6)) != RELPOS_OK) return st;
-  for (int i = 0; i < 5; ++i) {
-    if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
-  }
-  if ((st = check_device(ops, 6)) != RELPOS_OK) return st;
-
-  DeviceProps props{};
-  if (device_props(&props) != 0) return RELPOS_E_HIP;
-  auto fits = [&](int c) {
-    return relpos::attn_lds_bytes(c, static_cast<int>(H), static_cast<int>(W)) <=
-           static_cast<size_t>(props.lds_limit);
-  };
-  int cfg = forced_attn_config();
-  if (cfg < 0 || !fits(cfg)) cfg = attn_auto_config(BH, H * W, in_dtype == RELPOS_BF16, props.cus);
-  if (!fits(cfg)) {
-    cfg = -1;
-    for (int cand : kAttnFallback) {
-      if (fits(cand)) {
-        cfg = cand;
-        break;
-      }
-    }
-  }
-  if (cfg < 0) return RELPOS_E_SHAPE;
-
-  relpos::AttnArgs a{q, k, v, rel_h, rel_w, out,
-                     static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
-                     in_dtype == RELPOS_BF16, out_dtype == RELPOS_FP32};
-  if (relpos::launch_attn_fwd(a, cfg, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
-  return RELPOS_OK;
+relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                 const float* rel_h, const float* rel_w, void* out,
+                                 int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                 float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                 void* workspace, int64_t workspace_bytes, void* stream) {
+  if (workspace_bytes < 0) return RELPOS_E_VALUE;
+  return attn_fwd_impl(q, k, v, rel_h, rel_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
+                       true, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

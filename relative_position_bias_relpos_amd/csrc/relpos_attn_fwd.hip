@@ -4,8 +4,11 @@
 // block, no dense [N, N] bias).
 //
 // Work layout
-//   * A workgroup owns BM = 32*NW consecutive queries of one (batch, head);
-//     each of its NW waves owns 32 of them.
+//   * A unit is BM = 32*NW consecutive queries of one (batch, head); each of a
+//     workgroup's NW waves owns 32 of them.  Either one workgroup per unit
+//     takes all of the unit's key tiles, or (key-range split) a persistent
+//     grid of one workgroup per CU takes equal contiguous ranges of all
+//     (unit, tile) work, and units cut between ranges are merged afterwards.
 //   * Keys are visited in 2-D tiles of the key grid: 4 grid rows x 16 grid
 //     columns = 64 keys, in column bands (kw0 outer, kh0 inner).  Key o
 //     (0..63) of a tile is grid cell (kh0 + o/16, kw0 + o%16); cells outside
@@ -14,8 +17,8 @@
 //     holds one query (lane%32) and 32 of the tile's keys,
 //     o = 32*st + 8*g + 4*(lane/32) + e, i.e. grid offsets r = 2*st + g/2 and
 //     c = 8*(g%2) + 4*(lane/32) + e.  Its bias therefore needs 8 rel_w values
-//     per column band (kept in registers for the whole band) and 4 rel_h
-//     values per tile (prefetched from global memory one tile ahead).
+//     per column band, which initialise the first Q.K^T MFMA's accumulator,
+//     and 4 rel_h values per tile (prefetched one tile ahead).
 //   * O^T += V^T * P^T, again 32x32x16 MFMA, with P in fp16.  V tiles are kept
 //     row-major in LDS and read with the gfx950 transpose read
 //     (ds_read_b64_tr_b16), which hands each lane four consecutive keys of one
@@ -33,8 +36,9 @@
 //
 // Online softmax (exp2 domain, scores pre-multiplied by log2 e)
 //   * Each query row keeps a reference maximum m.  Per tile,
-//     p = exp2(s*scale*log2e + rel_w' + (rel_h' - m)); the fp16 values of p
-//     are summed (v_dot2) into l and fed to the P.V MFMA.
+//     p = exp2(fma(s + rel_w*log2e/c2, c2, rel_h*log2e - m)) with c2 =
+//     scale*log2e; the fp16 values of p are summed (v_dot2) into l and fed to
+//     the P.V MFMA.
 //   * m is only moved when it must be: on the first tile (exact tile maximum),
 //     and when some p of a tile exceeds 2^15, detected from the per-lane sum of
 //     the rounded p.  Then the tile's true maximum is taken, O and l are
@@ -52,12 +56,24 @@ namespace {
 
 using namespace attn;
 
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
+// A piece: a workgroup's partial result for one unit -- O (unnormalised,
+// BM x 64), then the reference maximum m and the row sum l of each query.
+// Unit i of the split last round keeps its head in slot 2i, its tail in 2i+1.
+template <int BM>
+constexpr int64_t piece_floats() {
+  return static_cast<int64_t>(BM) * kD + 2 * BM;
+}
+
+// One segment: tiles [t0, t0 + nt) of unit `unit`.  A full segment (nt == T)
+// writes the normalised output; otherwise the segment is one piece of a split
+// unit (see SplitPlan), written to workspace slot `slot`.
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
+__device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int q_tiles, float c2, float rw_mul) {
+    int H, int W, int q_tiles, float c2, float rw_mul,
+    float* __restrict__ ws, int unit, int t0, int nt, int slot) {
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
   const int N = H * W;
@@ -71,9 +87,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   const int wave = tid >> 6;
   const int half = lane >> 5;
 
-  const int work = xcd_work_index(static_cast<int>(gridDim.x));
-  const int bh = work / q_tiles;
-  const int q0 = (work - bh * q_tiles) * BM;
+  const int bh = unit / q_tiles;
+  const int q0 = (unit - bh * q_tiles) * BM;
   const size_t head = static_cast<size_t>(bh) * N;
 
   // ---- this lane's query: Q^T operand fragments (4 k-steps of 16) ----------
@@ -86,7 +101,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
                  : u32x4{0, 0, 0, 0};
   }
 
-  const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
+  const int T = nt;  // tiles of this segment
 
   // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
   constexpr int CH = (kTileKeys * kD / 8) / NT;  // 16-byte chunks of K (and of V) per thread
@@ -219,17 +234,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in LDS, tile 2 in registers, S of tile 0 ----
-  const TilePos p0{0, 0};
+  // ---- prologue: the segment's tiles 0 and 1 in LDS, tile 2 in registers,
+  // S of tile 0.  Tile t0 of the key walk (column bands of ceil(H/4) tiles).
+  const int band_tiles = (H + kTileRows - 1) / kTileRows;
+  const TilePos p0{(t0 % band_tiles) * kTileRows, (t0 / band_tiles) * kTileCols};
   const TilePos p1 = next_tile(p0, H);
   const TilePos p2 = next_tile(p1, H);
-  load_band(0);
+  load_band(p0.kw);
   load_tile(p0);
   store_tile(0);
-  load_tile(p1);  // tiles past the last one are staged too (from outside the grid) and never used
+  load_tile(p1);  // tiles past the segment's last one are staged too and never used
   store_tile(1);
   load_tile(p2);
-  load_rh(0);
+  load_rh(p0.kh);
   __syncthreads();
 
   acc[0] = f32x16{};
@@ -391,8 +408,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store ----
   const float lt = l + __shfl_xor(l, 32);
+  float inv = 1.0f / lt;
+  if constexpr (SPLIT) {
+    const int unit_tiles = band_tiles * ((W + kTileCols - 1) / kTileCols);
+    if (nt != unit_tiles) {
+      // One piece of a split unit: O (unnormalised), m and l go to the
+      // workspace; split_merge_kernel combines the pieces after this launch.
+      const int ql = wave * 32 + (lane & 31);  // query within the unit
+      float* pw = ws + static_cast<int64_t>(slot) * piece_floats<BM>();
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * half;
+          *reinterpret_cast<f32x4*>(pw + ql * kD + d) =
+              f32x4{acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+        }
+      if (half == 0) {
+        pw[BM * kD + ql] = m;
+        pw[BM * kD + BM + ql] = lt;
+      }
+      return;
+    }
+  }
   if (!qok) return;
-  const float inv = 1.0f / lt;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
@@ -411,37 +450,136 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED>
+// Without SPLIT: one workgroup per unit, all of its tiles.  With SPLIT: a
+// persistent grid following SplitPlan: full rounds of units, then the split
+// last round.
+
+// Merges the head and tail pieces of each unit of the split last round (head
+// first, so results are reproducible) and writes the normalised output.
+// Sixteen workgroups per unit, one thread per (query, 4-float chunk of d).
+template <bool BF16, bool OUT_F32>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ ws, void* __restrict__ out,
+                                                          int N, int q_tiles, int first_unit) {
+  constexpr int BM = 256;
+  const int ui = blockIdx.x >> 4;  // unit of the last round
+  const int unit = first_unit + ui;
+  const int it = ((blockIdx.x & 15) << 8) + threadIdx.x;  // 0 .. 4095
+  const int ql = it >> 4, c = 4 * (it & 15);
+  const int bh = unit / q_tiles;
+  const int qi = (unit - bh * q_tiles) * BM + ql;
+  if (qi >= N) return;
+  const float* ph = ws + (2 * static_cast<int64_t>(ui)) * piece_floats<BM>();
+  const float* pt = ph + piece_floats<BM>();
+  const float mh = ph[BM * kD + ql], mt = pt[BM * kD + ql];
+  const float lh = ph[BM * kD + BM + ql], lt = pt[BM * kD + BM + ql];
+  const f32x4 xh = *reinterpret_cast<const f32x4*>(ph + ql * kD + c);
+  const f32x4 xt = *reinterpret_cast<const f32x4*>(pt + ql * kD + c);
+  const float mx = __builtin_fmaxf(mh, mt);
+  const float wh = exp2_fast(mh - mx), wt = exp2_fast(mt - mx);
+  const float inv = 1.0f / (lh * wh + lt * wt);
+  f32x4 o4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o4[e] = (xh[e] * wh + xt[e] * wt) * inv;
+  const size_t row = static_cast<size_t>(bh) * N + qi;
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * kD + c) = o4;
+  } else {
+    const u32x2 pk = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
+                          : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + row * kD + c) = pk;
+  }
+}
+
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
+    const float* __restrict__ rel_w, void* __restrict__ out,
+    int H, int W, int q_tiles, float c2, float rw_mul,
+    float* __restrict__ ws, SplitPlan plan) {
+  const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
+  const int L = xcd_work_index(static_cast<int>(gridDim.x));
+  if constexpr (!SPLIT) {
+    attn_segment<BF16, OUT_F32, NW, ALIGNED, false>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
+                                                    ws, L, 0, T, 0);
+  } else {
+    const int P = static_cast<int>(gridDim.x);
+    for (int i = 0; i < plan.rounds; ++i) {
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
+                                                     ws, i * P + L, 0, T, 0);
+      __syncthreads();  // the next segment reuses the LDS ring
+    }
+    const int base = plan.rounds * P;
+    if (L < plan.rest) {
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
+                                                     ws, base + L, 0, plan.s, 2 * L);
+    } else if (plan.s < T) {
+      for (int j = 0; j < plan.k; ++j) {
+        const int ui = (L - plan.rest) * plan.k + j;
+        if (ui >= plan.rest) break;
+        attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
+                                                       ws, base + ui, plan.s, T - plan.s, 2 * ui + 1);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// Split workspace: two piece slots per workgroup.
+int64_t split_piece_bytes(int ctas) {
+  return 2 * static_cast<int64_t>(ctas) * piece_floats<256>() * static_cast<int64_t>(sizeof(float));
+}
+
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
 hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
-  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED>;
+  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
   constexpr int BM = 32 * NW;
   const int q_tiles = (a.H * a.W + BM - 1) / BM;
-  dim3 grid(static_cast<unsigned>(q_tiles * a.BH));
+  const int64_t units = static_cast<int64_t>(q_tiles) * a.BH;
+  const int64_t T = static_cast<int64_t>((a.W + kTileCols - 1) / kTileCols) * ((a.H + kTileRows - 1) / kTileRows);
+  float* ws = nullptr;
+  unsigned grid = static_cast<unsigned>(units);
+  SplitPlan plan{};
+  if constexpr (SPLIT) {
+    ws = static_cast<float*>(a.ws);
+    plan = split_plan(units, static_cast<int>(T), a.split_ctas);
+    grid = static_cast<unsigned>(a.split_ctas);
+  }
   const float c2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, q_tiles, c2, kLog2e / c2);
+                     a.H, a.W, q_tiles, c2, kLog2e / c2, ws, plan);
+  if constexpr (SPLIT) {
+    if (plan.rest > 0 && plan.s < T) {
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((split_merge_kernel<BF16, OUT_F32>), dim3(static_cast<unsigned>(plan.rest) * 16),
+                         dim3(256), 0, stream, static_cast<const float*>(ws), a.out, a.H * a.W, q_tiles,
+                         plan.rounds * a.split_ctas);
+    }
+  }
   return hipGetLastError();
 }
 
-template <bool BF16, bool OUT_F32, int NW>
+template <bool BF16, bool OUT_F32, int NW, bool SPLIT>
 hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
   // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch_cfg<BF16, OUT_F32, NW, true>(a, lds, stream)
-                 : launch_cfg<BF16, OUT_F32, NW, false>(a, lds, stream);
+  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT>(a, lds, stream)
+                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT>(a, lds, stream);
 }
 
 template <bool BF16, bool OUT_F32>
-hipError_t launch_dt(const AttnArgs& a, int nw, size_t lds, hipStream_t stream) {
-  switch (nw) {
-    case 8: return launch_nw<BF16, OUT_F32, 8>(a, lds, stream);
-    case 4: return launch_nw<BF16, OUT_F32, 4>(a, lds, stream);
-    default: return launch_nw<BF16, OUT_F32, 2>(a, lds, stream);
+hipError_t launch_dt(const AttnArgs& a, int cfg, size_t lds, hipStream_t stream) {
+  switch (cfg) {
+    case 0: return launch_nw<BF16, OUT_F32, 8, false>(a, lds, stream);
+    case 1: return launch_nw<BF16, OUT_F32, 4, false>(a, lds, stream);
+    case 2: return launch_nw<BF16, OUT_F32, 2, false>(a, lds, stream);
+    default: return launch_nw<BF16, OUT_F32, 8, true>(a, lds, stream);  // kAttnSplitConfig
   }
 }
 
@@ -449,22 +587,27 @@ size_t attn32_lds_bytes() { return 2 * kSlots * static_cast<size_t>(kTileHalves)
 
 }  // namespace
 
-int attn_num_configs() { return 5; }
+int attn_num_configs() { return 6; }
+
+size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas) {
+  (void)BH;
+  (void)N;
+  return static_cast<size_t>(split_piece_bytes(ctas));
+}
 
 size_t attn_lds_bytes(int cfg, int H, int W) {
   (void)H;
   (void)W;
-  return cfg >= 3 ? attn16_lds_bytes() : attn32_lds_bytes();
+  return cfg == 3 || cfg == 4 ? attn16_lds_bytes() : attn32_lds_bytes();
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
-  if (cfg >= 3) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
-  const int nw = cfg == 0 ? 8 : (cfg == 1 ? 4 : 2);
+  if (cfg == 3 || cfg == 4) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
   const size_t lds = attn32_lds_bytes();
   if (a.bf16) {
-    return a.out_f32 ? launch_dt<true, true>(a, nw, lds, stream) : launch_dt<true, false>(a, nw, lds, stream);
+    return a.out_f32 ? launch_dt<true, true>(a, cfg, lds, stream) : launch_dt<true, false>(a, cfg, lds, stream);
   }
-  return a.out_f32 ? launch_dt<false, true>(a, nw, lds, stream) : launch_dt<false, false>(a, nw, lds, stream);
+  return a.out_f32 ? launch_dt<false, true>(a, cfg, lds, stream) : launch_dt<false, false>(a, cfg, lds, stream);
 }
 
 }  // namespace relpos

@@ -30,15 +30,48 @@ struct AttnArgs {
   float scale;
   bool bf16;
   bool out_f32;
+  // Configuration kAttnSplitConfig only: a scratch workspace of
+  // attn_split_workspace_bytes(BH, H*W, split_ctas) bytes and the device's
+  // CU count.
+  void* ws = nullptr;
+  int split_ctas = 0;
 };
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
 // Attention launch configurations:
-//   0, 1, 2: 32 queries per wave, 8, 4 or 2 waves per workgroup (default: 0)
+//   0, 1, 2: 32 queries per wave, 8, 4 or 2 waves per workgroup, one
+//            workgroup per unit of 32*waves queries
 //   3: 16 queries per wave, 4 waves per workgroup (64 queries)
 //   4: 16 queries per wave, 8 waves per workgroup (128 queries)
+//   5: configuration 0 with the key range split over a persistent grid of
+//      split_ctas workgroups (needs the workspace)
+constexpr int kAttnSplitConfig = 5;
+
+// Last-round split of configuration kAttnSplitConfig.  With `units` query
+// units of T key tiles on P workgroups (one per CU), `rounds` = units / P full
+// rounds run unsplit; the rest = units % P units of the last round are cut at
+// key tile s: their heads [0, s) run on `rest` workgroups and their tails
+// [s, T) on the idle ones, k tails each, every head and every tail starting
+// at the same tile so a head's K/V tiles are shared in L2.  s = T*k/(k+1)
+// balances the two (k = ceil(rest / (P - rest))).  s == T means no tails
+// (T < 2): the last round then runs unsplit too.
+struct SplitPlan {
+  int rounds, rest, k, s;
+};
+inline SplitPlan split_plan(int64_t units, int T, int P) {
+  SplitPlan p{};
+  p.rounds = static_cast<int>(units / P);
+  p.rest = static_cast<int>(units - static_cast<int64_t>(p.rounds) * P);
+  if (p.rest == 0) return p;
+  p.k = (p.rest + (P - p.rest) - 1) / (P - p.rest);
+  p.s = static_cast<int>((static_cast<int64_t>(T) * p.k + (p.k + 1) / 2) / (p.k + 1));
+  if (p.s < 1) p.s = 1;
+  if (p.s > T - 1) p.s = T < 2 ? T : T - 1;
+  return p;
+}
 int attn_num_configs();
+size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas);
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);

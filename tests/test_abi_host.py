@@ -22,7 +22,7 @@ OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_DEVICE, E_ALIAS, E_LAUNCH, E_HIP, E_VAL
 
 def _declared():
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:relpos_status|const char\*|int)\s+(relpos_\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:relpos_status|const char\*|int64_t|int)\s+(relpos_\w+)\s*\(", text, re.M)
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +42,8 @@ def lib():
 
 def test_header_declares_the_calls():
     names = set(_declared())
-    assert {"relpos_build", "relpos_attn_fwd", "relpos_status_string", "relpos_abi_version"} <= names
+    assert {"relpos_build", "relpos_attn_fwd", "relpos_attn_fwd_ws", "relpos_attn_workspace_bytes",
+            "relpos_attn_config", "relpos_status_string", "relpos_abi_version"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -145,10 +146,16 @@ def test_aliasing(lib):
 
 # ---- launch configuration choice (host-only cost model) ----------------------
 
-def _cfg(lib, B, heads, H, W, dt, cus=256):
+def _cfg(lib, B, heads, H, W, dt, cus=256, ws=0):
     lib.relpos_attn_config.restype = ctypes.c_int
-    lib.relpos_attn_config.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
-    return lib.relpos_attn_config(B, heads, H, W, dt, cus)
+    lib.relpos_attn_config.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return lib.relpos_attn_config(B, heads, H, W, dt, cus, ws)
+
+
+def _ws_bytes(lib, B, heads, H, W, dt, cus=256):
+    lib.relpos_attn_workspace_bytes.restype = ctypes.c_int64
+    lib.relpos_attn_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
+    return lib.relpos_attn_workspace_bytes(B, heads, H, W, dt, cus)
 
 
 def test_attn_config_on_the_workloads(lib):
@@ -186,3 +193,59 @@ def test_attn_config_rejects_bad_input(lib):
     assert _cfg(lib, 1, 1, 0, 8, BF16) == -1
     assert _cfg(lib, 1, 1, 8, 8, FP32) == -1
     assert _cfg(lib, 1, 1, 8, 8, BF16, cus=0) == -1
+
+
+def test_attn_config_with_workspace(lib):
+    SPLIT = 5
+    # 64x64, 12 heads: 192 units of 64 tiles on 256 CUs, no full round; the
+    # 64 idle CUs take 3 tails each: s = 48, 0.95 * (48 + 4) / 64 = 0.77
+    # rounds against 0.95 unsplit -> split.
+    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == SPLIT
+    # 48x80, 2x12 heads: 360 units of 60 tiles: one full round, then 104
+    # units cut at s = 30: 0.95 * (1 + 34 / 60) = 1.49 against 1.77.
+    assert _cfg(lib, 2, 12, 48, 80, BF16, ws=1) == SPLIT
+    # 96x96, 2x16 heads: 1152 units of 144 tiles: 4 rounds, then 128 cut at
+    # s = 72: 0.95 * (4 + 76 / 144) = 4.30 < 4.75.
+    assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == SPLIT
+    # fp16 64x64, 4x12 heads: 768 units = 3 whole rounds; splitting gains nothing.
+    assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 1
+    # 16x16, 2 heads: 8 tiles in all, under 8 per CU -> no split.
+    assert _cfg(lib, 1, 2, 16, 16, BF16, ws=1) in (0, 1)
+    # without a workspace the split is never chosen
+    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=0) == 0
+
+
+def test_workspace_bytes(lib):
+    # two piece slots of (256*64 + 2*256) floats per compute unit
+    assert _ws_bytes(lib, 1, 12, 64, 64, BF16) == 256 * 2 * (256 * 64 + 512) * 4
+    # 64x64, 12 heads on 128 CUs: one full round of 128 units, then 64 units
+    # split at tile 32: 0.95 * (1 + (32 + 4) / 64) = 1.48 against 1.77.
+    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128, ws=1) == 5
+    assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=128) == 128 * 2 * (256 * 64 + 512) * 4
+    # 16x32 grid, 150 heads, 128 CUs: 300 units of 8 tiles, 2 rounds + 44
+    # split at tile 4: 0.95 * (2 + (4 + 4) / 8) = 2.85, no better than 2.77.
+    assert _cfg(lib, 1, 150, 16, 32, BF16, cus=128, ws=1) == 1
+    assert _ws_bytes(lib, 1, 150, 16, 32, BF16, cus=128) == 0
+    # no split chosen -> 0; bad input -> -1
+    assert _ws_bytes(lib, 4, 12, 64, 64, FP16) == 0
+    assert _ws_bytes(lib, 1, 12, 64, 64, FP32) == -1
+    assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=0) == -1
+
+
+def test_attn_fwd_ws_rejects_negative_workspace_size(lib):
+    f = lib.relpos_attn_fwd_ws
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    fake = [vp(0x100000 * (i + 1)) for i in range(6)]
+    assert f(*fake, 1, 1, 8, 8, 64, 0.125, BF16, FP32, vp(0x900000), -1, vp(0)) == E_VALUE
+    # the size checks still come first
+    assert f(*fake, 1, 1, 8, 8, 32, 0.125, BF16, FP32, vp(0x900000), 1024, vp(0)) == E_SHAPE
+
+
+def test_attn_fwd_grid_limit(lib):
+    # 65535 heads on a 4096x4096 grid: 2^18 workgroups of 64 queries per head
+    # overflow a 1-D grid -> E_SHAPE before any pointer is looked at.
+    vp = ctypes.c_void_p
+    assert lib.relpos_attn_fwd(vp(0), vp(0), vp(0), vp(0), vp(0), vp(0), 1, 65535, 4096, 4096, 64,
+                               0.125, BF16, FP32, vp(0)) == E_SHAPE

@@ -178,3 +178,86 @@ def test_automatic_config_matches_its_prediction(name, monkeypatch):
     monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
     forced, _, _ = G.gpu_run(d)
     assert torch.equal(auto, forced), (name, cfg)
+
+
+# ---- key-range split (relpos_attn_fwd_ws) ----------------------------------------
+
+def _split_ws_bytes():
+    """The workspace size documented in include/relpos.h for the split launch."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return cus * 2 * (256 * 64 + 2 * 256) * 4
+
+
+def _run_split(d, ws):
+    from relative_position_bias_relpos_amd import binding as rp
+    g = G.to_dev(d)
+    rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
+    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("tiny", dict(H=14, W=14)), ("tiny", dict(H=7, W=9, dtype="fp16")),
+                                     ("rect", dict(B=1, heads=3, H=21, W=35)),
+                                     ("batched_fp16", dict(B=1, heads=2, H=20, W=24))])
+def test_forced_split_full(name, kw, monkeypatch):
+    """Forced split on small grids: every unit is in the last round, cut into a
+    head and a tail (down to one tile each) that are merged afterwards."""
+    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
+    d = G.make(name, **kw)
+    ws = torch.full((_split_ws_bytes(),), 0x7f, dtype=torch.uint8, device="cuda")  # contents are not read
+    out = _run_split(d, ws)
+    ref, _, _ = G.oracle_full(d)
+    _check(f"split {name} {kw}", np.abs(G.f64(out) - ref))
+    again = _run_split(d, ws)
+    assert torch.equal(out, again), "split result depends on arrival order"
+
+
+@pytest.mark.parametrize("name,rows", [("deepencoder", 96), ("rect", 48), ("vitl", 32)])
+def test_split_full_size_sampled(name, rows, monkeypatch):
+    """The full-size workloads the cost model splits, in the benchmarked launch."""
+    monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
+    from relative_position_bias_relpos_amd import binding as rp
+    d = G.make(name)
+    B, nh = d["q"].shape[:2]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, cus) == 5
+    nbytes = rp.workspace_bytes(B, nh, d["H"], d["W"], d["q"].dtype, cus)
+    assert nbytes == _split_ws_bytes()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = _run_split(d, ws)
+    _check(f"{name} split sampled", G.oracle_sampled(d, out, rows))
+    # Each piece rounds p to fp16 against its own reference maximum, so the
+    # split and unsplit launches differ by rounding only (both meet the bar).
+    unsplit = _run_split(d, None)
+    assert (out - unsplit).abs().max().item() <= G.MAX_ABS
+    for _ in range(2):
+        assert torch.equal(out, _run_split(d, ws))
+
+
+def test_split_workspace_errors(monkeypatch):
+    from relative_position_bias_relpos_amd import binding as rp
+    monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
+    d = G.make("deepencoder", B=1, heads=12)
+    g = G.to_dev(d)
+    rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
+    small = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rp.RelposError) as e:
+        rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=small)
+    assert e.value.status == 2  # E_SHAPE: workspace too small
+    big = torch.zeros(_split_ws_bytes() + g["q"].numel() * 4, dtype=torch.uint8, device="cuda")
+    out = big[: g["q"].numel() * 4].view(torch.float32).view(g["q"].shape)
+    with pytest.raises(rp.RelposError) as e:
+        rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], out=out, workspace=big)
+    assert e.value.status == 6  # E_ALIAS: the workspace overlaps out
+
+
+def test_split_workspace_reused_across_shapes(monkeypatch):
+    """One workspace for split problems of different shapes in turn."""
+    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
+    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda")
+    for d in (G.make("deepencoder", B=1, heads=2), G.make("rect", B=1, heads=6), G.make("deepencoder", B=1, heads=2)):
+        out = _run_split(d, ws)
+        unsplit = _run_split(d, None)
+        assert (out - unsplit).abs().max().item() <= G.MAX_ABS
+        assert torch.equal(out, _run_split(d, ws))
