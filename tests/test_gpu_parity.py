@@ -261,3 +261,23 @@ def test_split_workspace_reused_across_shapes(monkeypatch):
         unsplit = _run_split(d, None)
         assert (out - unsplit).abs().max().item() <= G.MAX_ABS
         assert torch.equal(out, _run_split(d, ws))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_forced_split_half_precision_output(dtype, monkeypatch):
+    """The merge kernel's bf16/fp16 stores, against the oracle."""
+    from relative_position_bias_relpos_amd import binding as rp
+    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
+    d = G.make("tiny", dtype=dtype, H=14, W=18)
+    g = G.to_dev(d)
+    rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
+    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda")
+    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"],
+                             out_dtype=g["q"].dtype, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.dtype == g["q"].dtype
+    ref, _, _ = G.oracle_full(d)
+    err = np.abs(G.f64(out) - ref)
+    ulp = 2.0 ** (-8 if dtype == "bf16" else -11)
+    assert (err <= G.MAX_ABS + ulp * np.abs(ref)).all(), dtype
+    print(f"[parity] split tiny 14x18 out={dtype}: max={err.max():.3e} mean={err.mean():.3e}", flush=True)
