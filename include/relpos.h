@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 2
+#define RELPOS_ABI_VERSION 3
 
 typedef enum relpos_dtype {
   RELPOS_BF16 = 0,
@@ -170,6 +170,52 @@ relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
  */
 int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W,
                                     relpos_dtype in_dtype, int cu_count);
+
+/*
+ * relpos_attn_fused: relpos_build followed by relpos_attn_fwd in one launch,
+ * without the rel_h / rel_w tensors (the fusion the PR #55629 page's
+ * implementation section leaves to the model helper: there rel_h and rel_w are
+ * built by add_decomposed_rel_pos before the fused kernel is called).
+ *
+ * Defines the same `out` as relpos_build + relpos_attn_fwd on the same inputs
+ * (same tolerance against the definition; results differ from the two-call
+ * path by rounding only).  Each workgroup computes the bias rows of its 256
+ * queries from q and the tables on MFMA (fp32 accumulation, as relpos_build),
+ * keeps them in its slot of the workspace and reads them back per key tile.
+ * The launch is the persistent split launch of relpos_attn_fwd_ws (one 8-wave
+ * workgroup per compute unit, last round split, merge kernel when split).
+ *
+ * Arguments: q, k, v, out, B, heads, H, W, D, scale, in_dtype, out_dtype and
+ * stream as for relpos_attn_fwd, plus
+ *   rel_pos_h  [2H-1, D]  in_dtype (device)
+ *   rel_pos_w  [2W-1, D]  in_dtype (device)
+ *   workspace  device scratch, 16-byte aligned, not overlapping any other
+ *              operand; contents on entry are not read.  Calls sharing a
+ *              workspace must not run concurrently.
+ *   workspace_bytes  >= relpos_fused_workspace_bytes(...) for the current
+ *              device (else E_SHAPE); negative is E_VALUE.
+ * Errors: E_SHAPE, E_DTYPE, E_VALUE, E_NULL, E_ALIGN, E_ALIAS (out or the
+ * workspace overlapping another operand), E_DEVICE, E_HIP (device query),
+ * E_LAUNCH.  Check order: sizes, dtypes, scalars; then (B*heads > 0) NULL and
+ * alignment of all seven pointers, out overlapping an input; then the
+ * device's compute-unit count is queried, and the workspace size (E_SHAPE),
+ * workspace overlap and device memory of every operand are checked.
+ */
+relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
+                                const void* rel_pos_h, const void* rel_pos_w, void* out,
+                                int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * relpos_fused_workspace_bytes: workspace bytes relpos_attn_fused needs on a
+ * device with `cu_count` compute units:
+ *   cu_count * (2 * (256*64 + 2*256) + 256 * (roundup(H, 4) + roundup(W, 16))) * 4
+ * (two split pieces and one slot of bias rows per workgroup).  -1 if a size
+ * or the dtype is out of range or cu_count < 1.  Host-only.
+ */
+int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W,
+                                     relpos_dtype in_dtype, int cu_count);
 
 /*
  * relpos_attn_config: the launch configuration relpos_attn_fwd (with_workspace

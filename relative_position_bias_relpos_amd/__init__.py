@@ -5,7 +5,8 @@ declared in ``include/relpos.h``).  This package is a thin ctypes binding with t
 same names; it only marshals torch tensors (device memory) and the current stream.
 """
 
-__all__ = ["relpos_build", "relpos_attn_fwd", "attn_config", "workspace_bytes", "status_string",
+__all__ = ["relpos_build", "relpos_attn_fwd", "relpos_attn_fused", "attn_config", "workspace_bytes",
+           "fused_workspace_bytes", "status_string",
            "abi_version", "library_path"]
 
 

@@ -55,6 +55,11 @@ def _load():
                                            vp, i64, vp]
         lib.relpos_attn_workspace_bytes.restype = i64
         lib.relpos_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+        lib.relpos_attn_fused.restype = i32
+        lib.relpos_attn_fused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32,
+                                          vp, i64, vp]
+        lib.relpos_fused_workspace_bytes.restype = i64
+        lib.relpos_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         lib.relpos_attn_config.restype = i32
         lib.relpos_attn_config.argtypes = [i64, i64, i64, i64, i32, i32, i32]
         _lib = lib
@@ -85,6 +90,14 @@ def workspace_bytes(B, heads, H, W, dtype, cu_count):
     n = _load().relpos_attn_workspace_bytes(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count))
     if n < 0:
         raise ValueError("sizes or dtype out of range for relpos_attn_fwd")
+    return n
+
+
+def fused_workspace_bytes(B, heads, H, W, dtype, cu_count):
+    """Bytes of workspace relpos_attn_fused needs on `cu_count` compute units."""
+    n = _load().relpos_fused_workspace_bytes(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count))
+    if n < 0:
+        raise ValueError("sizes or dtype out of range for relpos_attn_fused")
     return n
 
 
@@ -206,4 +219,43 @@ def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torc
                                 B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
                                 ws_ptr, ws_len, _stream(q))
     _check("relpos_attn_fwd_ws", st)
+    return out
+
+
+def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_dtype=torch.float32,
+                      workspace="auto"):
+    """relpos_build and relpos_attn_fwd in one launch: out [B,heads,H*W,D] from
+    q, k, v and the tables, without rel_h/rel_w tensors.
+
+    workspace: "auto" (default) uses a scratch workspace cached per (device,
+    stream); a tensor is used as the workspace.
+    """
+    lib = _load()
+    B, nh, D = _dims(q, H, W)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v must be bfloat16 or float16")
+    _need(rel_pos_h, "rel_pos_h", q.dtype)
+    _need(rel_pos_w, "rel_pos_w", q.dtype)
+    if tuple(rel_pos_h.shape) != (2 * H - 1, D) or tuple(rel_pos_w.shape) != (2 * W - 1, D):
+        raise ValueError("rel_pos_h/rel_pos_w must be [2H-1, D] and [2W-1, D]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need(out, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto" or a tensor')
+        need = fused_workspace_bytes(B, nh, H, W, q.dtype, _cu_count(q.device))
+        workspace = _cached_workspace(q.device, _stream(q).value, need)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError('workspace must be "auto" or a tensor')
+    st = lib.relpos_attn_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(out),
+                               B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    _check("relpos_attn_fused", st)
     return out

@@ -307,6 +307,70 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
   return static_cast<int64_t>(relpos::attn_split_workspace_bytes(BH, H * W, cu_count));
 }
 
+int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
+                                     int cu_count) {
+  int64_t BH = 0;
+  if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
+  return static_cast<int64_t>(relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W),
+                                                                 cu_count));
+}
+
+relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
+                                const void* rel_pos_h, const void* rel_pos_w, void* out,
+                                int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t BH = 0;
+  relpos_status st = check_dims(B, heads, H, W, D, &BH);
+  if (st != RELPOS_OK) return st;
+  if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
+  if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
+  if (!std::isfinite(scale) || workspace_bytes < 0) return RELPOS_E_VALUE;
+  if (BH == 0) return RELPOS_OK;
+  if (BH * ((H * W + 63) / 64) >= (int64_t(1) << 31)) return RELPOS_E_SHAPE;
+
+  const size_t N = static_cast<size_t>(H * W);
+  const size_t in_bytes = BH * N * 64 * 2;
+  const size_t out_bytes = BH * N * 64 * (out_dtype == RELPOS_FP32 ? 4 : 2);
+  Operand ops[7] = {
+      {q, in_bytes},
+      {k, in_bytes},
+      {v, in_bytes},
+      {rel_pos_h, static_cast<size_t>(2 * H - 1) * 64 * 2},
+      {rel_pos_w, static_cast<size_t>(2 * W - 1) * 64 * 2},
+      {out, out_bytes},
+      {workspace, 0},
+  };
+  if ((st = check_align(ops, 7)) != RELPOS_OK) return st;
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
+  }
+  // The workspace size depends on the device's compute-unit count.
+  DeviceProps props{};
+  if (device_props(&props) != 0) return RELPOS_E_HIP;
+  const size_t need = relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W), props.cus);
+  if (static_cast<uint64_t>(workspace_bytes) < need) return RELPOS_E_SHAPE;
+  ops[6].bytes = need;
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(ops[6], ops[i])) return RELPOS_E_ALIAS;
+  }
+  if (relpos::attn_lds_bytes(relpos::kAttnSplitConfig, static_cast<int>(H), static_cast<int>(W)) >
+      static_cast<size_t>(props.lds_limit)) {
+    return RELPOS_E_SHAPE;
+  }
+  if ((st = check_device(ops, 7)) != RELPOS_OK) return st;
+
+  relpos::AttnArgs a{q, k, v, nullptr, nullptr, out,
+                     static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
+                     in_dtype == RELPOS_BF16, out_dtype == RELPOS_FP32};
+  a.ws = workspace;
+  a.split_ctas = props.cus;
+  a.th = rel_pos_h;
+  a.tw = rel_pos_w;
+  if (relpos::launch_attn_fused(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  return RELPOS_OK;
+}
+
 relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
                                  const float* rel_h, const float* rel_w, void* out,
                                  int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,

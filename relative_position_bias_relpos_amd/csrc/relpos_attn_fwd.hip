@@ -56,6 +56,86 @@ namespace {
 
 using namespace attn;
 
+// ---- bias computed in the attention kernel ----------------------------------
+// One axis of the bias for the 32 queries of a wave: out[j][x] = q_j . T[a_j + L
+// - 1 - x] for x in [0, L), with a_j the query's coordinate along the axis
+// (qh for rel_h, qw for rel_w) and T the table of 2L - 1 rows (PR #55629 page,
+// key source snippet: add_decomposed_rel_pos on the unscaled q).  The products
+// C[j][r] = q_j . T[r] are taken on MFMA for 32 table rows at a time over the
+// rows [r_lo, r_hi] the wave's queries use, with A = the wave's Q fragments and
+// B = T^T; a lane then holds table row r for 16 queries and writes each value
+// to its diagonal position x = a_j + L - 1 - r.  For one query the 32 lanes of
+// a half write 32 consecutive floats.  Stores outside [0, L) are dropped by the
+// buffer range check (offset kOob).
+//
+// The queries' coordinates: query j_i = 8*(i/4) + 4*half + i%4 (the row of
+// result register i) is gq0 + min(j_i, jmax) with grid column t = qw0 + min(j_i,
+// jmax) < W + 32 past the wave's first grid row qh0; floor(t / W) is exact from
+// the float product (the quotient is at least 0.5/W from the next integer).
+template <bool BF16, bool AXIS_W>
+__device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* __restrict__ tab, int L,
+                                          int qh0, int qw0, int jmax, int W, float rcp_w, int r_lo, int r_hi,
+                                          float* dst, int Ls, int lane) {
+  // The empty asm makes the lane index opaque, so the per-register offsets
+  // below are recomputed here rather than hoisted out of the workgroup's
+  // loop over segments (where they would only take registers from it).
+  __asm__ volatile("" : "+v"(lane));
+  const int half = lane >> 5;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, static_cast<uint32_t>(32 * Ls) * 4);
+  int xa[16];  // a_i + L - 1: the position x of table row r = 0
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = 8 * (i >> 2) + 4 * half + (i & 3);
+    const int t = qw0 + (j < jmax ? j : jmax);
+    const int d = static_cast<int>((static_cast<float>(t) + 0.5f) * rcp_w);
+    xa[i] = (AXIS_W ? t - d * W : qh0 + d) + L - 1;
+  }
+  for (int rb = r_lo; rb <= r_hi; rb += 32) {
+    const int r = rb + (lane & 31);
+    const bool ok = r <= 2 * L - 2;
+    u32x4 tf[4];
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      tf[kd] = ok ? *reinterpret_cast<const u32x4*>(tab + static_cast<size_t>(r) * kD + 16 * kd + 8 * half)
+                  : u32x4{0, 0, 0, 0};
+    }
+    f32x16 c = {};
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) c = mfma32<BF16>(qf[kd], tf[kd], c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int x = xa[i] - r;
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      const int off = static_cast<unsigned>(x) < static_cast<unsigned>(L) ? 4 * (row * Ls + x) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b32(as_uint(c[i]), rs, off, 0, 0);
+    }
+  }
+}
+
+// rel_h and rel_w rows of the wave's 32 queries gq0 .. gq0+31 (clamped to the
+// last query, so rows of queries past the grid hold finite copies), written to
+// sh[j][0..H) and sw[j][0..W) with row strides Hs >= H and Ws >= W; the columns
+// [H, Hs) and [W, Ws) are set to -inf (keys outside the grid).  gq0 is
+// wave-uniform.
+template <bool BF16>
+__device__ __forceinline__ void fused_bias_rows(const u32x4 (&qf)[4], const uint16_t* __restrict__ th,
+                                                const uint16_t* __restrict__ tw, float* sh, float* sw,
+                                                int H, int W, int Hs, int Ws, int gq0, int N, int lane) {
+  const int half = lane >> 5;
+  const int ga = gq0 < N - 1 ? gq0 : N - 1;
+  const int gb = gq0 + 31 < N - 1 ? gq0 + 31 : N - 1;
+  const int qh0 = ga / W, qw0 = ga - qh0 * W;
+  const int qh1 = gb / W, qw1 = gb - qh1 * W;
+  const float rcp_w = 1.0f / static_cast<float>(W);
+  bias_axis<BF16, false>(qf, th, H, qh0, qw0, gb - ga, W, rcp_w, qh0, qh1 + H - 1, sh, Hs, lane);
+  // A wave that wraps to a new grid row holds every qw.
+  const int rw_lo = qh0 == qh1 ? qw0 : 0, rw_hi = qh0 == qh1 ? qw1 + W - 1 : 2 * W - 2;
+  bias_axis<BF16, true>(qf, tw, W, qh0, qw0, gb - ga, W, rcp_w, rw_lo, rw_hi, sw, Ws, lane);
+  const int j = lane & 31;
+  for (int p = H + half; p < Hs; p += 2) sh[j * Hs + p] = -__builtin_inff();
+  for (int p = W + half; p < Ws; p += 2) sw[j * Ws + p] = -__builtin_inff();
+}
+
 // A piece: a workgroup's partial result for one unit -- O (unnormalised,
 // BM x 64), then the reference maximum m and the row sum l of each query.
 // Unit i of the split last round keeps its head in slot 2i, its tail in 2i+1.
@@ -64,16 +144,25 @@ constexpr int64_t piece_floats() {
   return static_cast<int64_t>(BM) * kD + 2 * BM;
 }
 
+// Floats of one query's bias rows when computed in the kernel: rel_h padded
+// to whole 4-row tiles, rel_w to whole 16-column tiles.
+__host__ __device__ constexpr int fused_row_floats(int H, int W) {
+  return (H + kTileRows - 1) / kTileRows * kTileRows + (W + kTileCols - 1) / kTileCols * kTileCols;
+}
+
 // One segment: tiles [t0, t0 + nt) of unit `unit`.  A full segment (nt == T)
 // writes the normalised output; otherwise the segment is one piece of a split
-// unit (see SplitPlan), written to workspace slot `slot`.
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
+// unit (see SplitPlan), written to workspace slot `slot`.  FUSED: the bias rows
+// are computed from q and the tables th/tw into `bias_slot` (the workgroup's
+// BM * (Hs + Ws) floats) instead of being read from rel_h/rel_w.
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED>
 __device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
     int H, int W, int q_tiles, float c2, float rw_mul,
-    float* __restrict__ ws, int unit, int t0, int nt, int slot) {
+    float* __restrict__ ws, int unit, int t0, int nt, int slot,
+    const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw, float* bias_slot) {
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
   const int N = H * W;
@@ -165,20 +254,47 @@ __device__ __forceinline__ void attn_segment(
   // in both grid rows of a half), so after the multiply by c2 below the score
   // already carries its rel_w term.  rel_h (4 grid rows per tile) is
   // prefetched one tile ahead and added with the running maximum in one fma.
-  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
-  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
-  const int qrow = qok ? qi : 0;
-  const int rw_lane = (qrow * W + 4 * half) * 4;  // bytes: this lane's row, column 4*half
-  const int rh_lane = qrow * H * 4;
+  // The unit's bias rows (queries q0 .. q0+BM-1) have row strides hs and wst
+  // floats.  They are padded (whole tiles, 16-byte rows) when the grid is
+  // tile-aligned or when they are computed here (-inf columns past the grid):
+  // then each load is one 16-byte load without a mask.
+  constexpr bool kPadded = FUSED || ALIGNED;
+  int hs = H, wst = W;
+  const float* rh_rows;
+  const float* rw_rows;
+  int rows;
+  if constexpr (FUSED) {
+    hs = (H + kTileRows - 1) / kTileRows * kTileRows;
+    wst = (W + kTileCols - 1) / kTileCols * kTileCols;
+    rh_rows = bias_slot;
+    rw_rows = bias_slot + BM * hs;
+    rows = BM;
+  } else {
+    rh_rows = rel_h + (head + q0) * H;
+    rw_rows = rel_w + (head + q0) * W;
+    rows = N - q0 < BM ? N - q0 : BM;
+  }
+  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rw_rows, static_cast<uint32_t>(rows * wst) * 4);
+  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rh_rows, static_cast<uint32_t>(rows * hs) * 4);
+  const int ql = wave * 32 + (lane & 31);  // query within the unit
+  const int qrow = FUSED || qok ? ql : 0;
+  const int rw_lane = (qrow * wst + 4 * half) * 4;  // bytes: this lane's row, column 4*half
+  const int rh_lane = qrow * hs * 4;
   f32x16 rwc;
   auto load_band = [&](int kw0) {
     float x[8];
+    if constexpr (kPadded) {
+      const u32x4 a0 = buf_load16(rwrs, rw_lane, 4 * kw0);
+      const u32x4 a1 = buf_load16(rwrs, rw_lane + 32, 4 * kw0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int dc = 8 * (i >> 2) + (i & 3);  // column offset beyond 4*half
-      if constexpr (ALIGNED) {
-        x[i] = buf_loadf(rwrs, rw_lane + 4 * dc, 4 * kw0) * rw_mul;
-      } else {
+      for (int i = 0; i < 4; ++i) {
+        x[i] = as_float(a0[i]) * rw_mul;
+        x[4 + i] = as_float(a1[i]) * rw_mul;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int dc = 8 * (i >> 2) + (i & 3);  // column offset beyond 4*half
         const int c = kw0 + dc + 4 * half;
         const float y = buf_loadf(rwrs, c < W ? rw_lane + 4 * (kw0 + dc) : kOob);
         x[i] = c < W ? y * rw_mul : -__builtin_inff();
@@ -189,11 +305,13 @@ __device__ __forceinline__ void attn_segment(
   };
   float rhn[4];  // rel_h of the next tile's 4 grid rows (-inf outside the grid)
   auto load_rh = [&](int kh0) {
+    if constexpr (kPadded) {
+      const u32x4 a = buf_load16(rhrs, rh_lane, 4 * kh0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (ALIGNED) {
-        rhn[r] = buf_loadf(rhrs, rh_lane + 4 * r, 4 * kh0);
-      } else {
+      for (int r = 0; r < 4; ++r) rhn[r] = as_float(a[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
         const float y = buf_loadf(rhrs, kh0 + r < H ? rh_lane + 4 * (kh0 + r) : kOob);
         rhn[r] = kh0 + r < H ? y : -__builtin_inff();
       }
@@ -240,13 +358,29 @@ __device__ __forceinline__ void attn_segment(
   const TilePos p0{(t0 % band_tiles) * kTileRows, (t0 / band_tiles) * kTileCols};
   const TilePos p1 = next_tile(p0, H);
   const TilePos p2 = next_tile(p1, H);
-  load_band(p0.kw);
-  load_tile(p0);
-  store_tile(0);
-  load_tile(p1);  // tiles past the segment's last one are staged too and never used
-  store_tile(1);
-  load_tile(p2);
-  load_rh(p0.kh);
+  if constexpr (FUSED) {
+    // This wave's 32 bias rows; the wave reads back only its own rows, so
+    // waiting for its stores (vmcnt also counts stores) is enough.
+    const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar addresses
+    fused_bias_rows<BF16>(qf, th, tw, bias_slot + wu * 32 * hs, bias_slot + BM * hs + wu * 32 * wst,
+                          H, W, hs, wst, q0 + wu * 32, N, lane);
+    load_tile(p0);
+    store_tile(0);
+    load_tile(p1);
+    store_tile(1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    load_band(p0.kw);
+    load_tile(p2);
+    load_rh(p0.kh);
+  } else {
+    load_band(p0.kw);
+    load_tile(p0);
+    store_tile(0);
+    load_tile(p1);  // tiles past the segment's last one are staged too and never used
+    store_tile(1);
+    load_tile(p2);
+    load_rh(p0.kh);
+  }
   __syncthreads();
 
   acc[0] = f32x16{};
@@ -414,7 +548,6 @@ __device__ __forceinline__ void attn_segment(
     if (nt != unit_tiles) {
       // One piece of a split unit: O (unnormalised), m and l go to the
       // workspace; split_merge_kernel combines the pieces after this launch.
-      const int ql = wave * 32 + (lane & 31);  // query within the unit
       float* pw = ws + static_cast<int64_t>(slot) * piece_floats<BM>();
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
@@ -490,35 +623,48 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
   }
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
+// FUSED (always with SPLIT): the bias is computed per segment from q and the
+// tables th/tw; workgroup b keeps its bias rows in the workspace after the
+// 2 * P split pieces, at bias slot b.
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
     int H, int W, int q_tiles, float c2, float rw_mul,
-    float* __restrict__ ws, SplitPlan plan) {
+    float* __restrict__ ws, SplitPlan plan,
+    const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw) {
+  static_assert(!FUSED || SPLIT, "the fused bias needs the persistent grid");
+  constexpr int BM = 32 * NW;
   const int T = ((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows);
   const int L = xcd_work_index(static_cast<int>(gridDim.x));
+  float* bias_slot = nullptr;
+  if constexpr (FUSED) {
+    const int64_t slot_floats = static_cast<int64_t>(BM) * (fused_row_floats(H, W));
+    bias_slot = ws + 2 * static_cast<int64_t>(gridDim.x) * piece_floats<BM>() + blockIdx.x * slot_floats;
+  }
   if constexpr (!SPLIT) {
-    attn_segment<BF16, OUT_F32, NW, ALIGNED, false>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
-                                                    ws, L, 0, T, 0);
+    attn_segment<BF16, OUT_F32, NW, ALIGNED, false, false>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+                                                           rw_mul, ws, L, 0, T, 0, th, tw, bias_slot);
   } else {
     const int P = static_cast<int>(gridDim.x);
     for (int i = 0; i < plan.rounds; ++i) {
-      attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
-                                                     ws, i * P + L, 0, T, 0);
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+                                                            rw_mul, ws, i * P + L, 0, T, 0, th, tw, bias_slot);
       __syncthreads();  // the next segment reuses the LDS ring
     }
     const int base = plan.rounds * P;
     if (L < plan.rest) {
-      attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
-                                                     ws, base + L, 0, plan.s, 2 * L);
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+                                                            rw_mul, ws, base + L, 0, plan.s, 2 * L, th, tw,
+                                                            bias_slot);
     } else if (plan.s < T) {
       for (int j = 0; j < plan.k; ++j) {
         const int ui = (L - plan.rest) * plan.k + j;
         if (ui >= plan.rest) break;
-        attn_segment<BF16, OUT_F32, NW, ALIGNED, true>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2, rw_mul,
-                                                       ws, base + ui, plan.s, T - plan.s, 2 * ui + 1);
+        attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+                                                              rw_mul, ws, base + ui, plan.s, T - plan.s,
+                                                              2 * ui + 1, th, tw, bias_slot);
         __syncthreads();
       }
     }
@@ -530,9 +676,9 @@ int64_t split_piece_bytes(int ctas) {
   return 2 * static_cast<int64_t>(ctas) * piece_floats<256>() * static_cast<int64_t>(sizeof(float));
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT>
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED = false>
 hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
-  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT>;
+  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT, FUSED>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
@@ -552,7 +698,8 @@ hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, q_tiles, c2, kLog2e / c2, ws, plan);
+                     a.H, a.W, q_tiles, c2, kLog2e / c2, ws, plan,
+                     static_cast<const uint16_t*>(a.th), static_cast<const uint16_t*>(a.tw));
   if constexpr (SPLIT) {
     if (plan.rest > 0 && plan.s < T) {
       err = hipGetLastError();
@@ -565,12 +712,12 @@ hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool SPLIT>
+template <bool BF16, bool OUT_F32, int NW, bool SPLIT, bool FUSED = false>
 hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
   // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT>(a, lds, stream)
-                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT>(a, lds, stream);
+  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED>(a, lds, stream)
+                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED>(a, lds, stream);
 }
 
 template <bool BF16, bool OUT_F32>
@@ -593,6 +740,21 @@ size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas) {
   (void)BH;
   (void)N;
   return static_cast<size_t>(split_piece_bytes(ctas));
+}
+
+size_t attn_fused_workspace_bytes(int H, int W, int ctas) {
+  return static_cast<size_t>(split_piece_bytes(ctas)) +
+         static_cast<size_t>(ctas) * 256 * static_cast<size_t>(fused_row_floats(H, W)) * sizeof(float);
+}
+
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream) {
+  const size_t lds = attn32_lds_bytes();
+  if (a.bf16) {
+    return a.out_f32 ? launch_nw<true, true, 8, true, true>(a, lds, stream)
+                     : launch_nw<true, false, 8, true, true>(a, lds, stream);
+  }
+  return a.out_f32 ? launch_nw<false, true, 8, true, true>(a, lds, stream)
+                   : launch_nw<false, false, 8, true, true>(a, lds, stream);
 }
 
 size_t attn_lds_bytes(int cfg, int H, int W) {

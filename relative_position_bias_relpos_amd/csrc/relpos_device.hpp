@@ -33,6 +33,12 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// Bit casts through a by-value argument.  Apply these (not __builtin_bit_cast)
+// to an element of an ext_vector: this compiler lowers a bit cast of a vector
+// element expression as a read of the vector's first element.
+__device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+__device__ __forceinline__ uint32_t as_uint(float x) { return __builtin_bit_cast(uint32_t, x); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 

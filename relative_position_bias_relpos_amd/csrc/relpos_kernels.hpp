@@ -35,6 +35,10 @@ struct AttnArgs {
   // CU count.
   void* ws = nullptr;
   int split_ctas = 0;
+  // launch_attn_fused only: the tables rel_pos_h [2H-1, 64] and rel_pos_w
+  // [2W-1, 64] in the input dtype (rel_h and rel_w are then unused).
+  const void* th = nullptr;
+  const void* tw = nullptr;
 };
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
@@ -72,6 +76,11 @@ inline SplitPlan split_plan(int64_t units, int T, int P) {
 }
 int attn_num_configs();
 size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas);
+// The fused path: configuration kAttnSplitConfig's kernel with the bias
+// computed in the kernel.  Workspace: the split pieces, then one slot of bias
+// rows per workgroup (split_ctas workgroups).
+size_t attn_fused_workspace_bytes(int H, int W, int ctas);
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream);
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);

@@ -249,3 +249,68 @@ def test_attn_fwd_grid_limit(lib):
     vp = ctypes.c_void_p
     assert lib.relpos_attn_fwd(vp(0), vp(0), vp(0), vp(0), vp(0), vp(0), 1, 65535, 4096, 4096, 64,
                                0.125, BF16, FP32, vp(0)) == E_SHAPE
+
+
+# ---- relpos_attn_fused (host-side checks) ---------------------------------------
+
+def _fused(lib, ptrs=None, B=1, nh=2, H=4, W=4, D=64, scale=0.125, ind=BF16, outd=FP32, ws_bytes=1 << 30):
+    f = lib.relpos_attn_fused
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    p = ptrs or (P + [0x10000 * 7])
+    return f(*[vp(x) if x is not None else vp(0) for x in p[:6]], B, nh, H, W, D, scale, ind, outd,
+             vp(p[6]) if p[6] is not None else vp(0), ws_bytes, vp(0))
+
+
+def _fused_ws(lib, B, heads, H, W, dt, cus=256):
+    f = lib.relpos_fused_workspace_bytes
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int]
+    return f(B, heads, H, W, dt, cus)
+
+
+def test_fused_workspace_bytes(lib):
+    piece = 2 * (256 * 64 + 2 * 256)
+    # 64x64: rows padded to 64 + 64 floats per query, 256 queries per slot
+    assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 256 * (piece + 256 * 128) * 4
+    # 48x80 -> 48 + 80; 7x9 -> 8 + 16; 1x1 -> 4 + 16
+    assert _fused_ws(lib, 2, 12, 48, 80, BF16, cus=128) == 128 * (piece + 256 * 128) * 4
+    assert _fused_ws(lib, 1, 1, 7, 9, FP16, cus=8) == 8 * (piece + 256 * 24) * 4
+    assert _fused_ws(lib, 1, 1, 1, 1, BF16, cus=1) == (piece + 256 * 20) * 4
+    assert _fused_ws(lib, 1, 1, 8, 8, FP32) == -1
+    assert _fused_ws(lib, 1, 1, 0, 8, BF16) == -1
+    assert _fused_ws(lib, 1, 1, 8, 8, BF16, cus=0) == -1
+
+
+def test_fused_argument_errors(lib):
+    # sizes, dtypes and scalars come first (no pointer is looked at)
+    assert _fused(lib, D=32) == E_SHAPE
+    assert _fused(lib, H=0) == E_SHAPE
+    assert _fused(lib, ind=FP32) == E_DTYPE
+    assert _fused(lib, ind=BF16, outd=FP16) == E_DTYPE
+    assert _fused(lib, scale=float("nan")) == E_VALUE
+    assert _fused(lib, ws_bytes=-1) == E_VALUE
+    assert _fused(lib, ptrs=[None] * 7, B=0) == OK
+
+
+def test_fused_is_declared_with_its_workspace_query():
+    names = set(_declared())
+    assert {"relpos_attn_fused", "relpos_fused_workspace_bytes"} <= names
+
+
+def test_fused_pointer_errors(lib):
+    base = P + [0x10000 * 7]
+    for i in range(7):
+        p = list(base)
+        p[i] = None
+        assert _fused(lib, ptrs=p) == E_NULL, i
+        p = list(base)
+        p[i] += 4
+        assert _fused(lib, ptrs=p) == E_ALIGN, i
+    p = list(base)
+    p[5] = p[0]  # out == q
+    assert _fused(lib, ptrs=p) == E_ALIAS
+    p = list(base)
+    p[5] = p[3]  # out over rel_pos_h
+    assert _fused(lib, ptrs=p) == E_ALIAS
