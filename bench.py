@@ -2,7 +2,9 @@
 
 One step = relpos_build (rel_h/rel_w from q and the tables) followed by
 relpos_attn_fwd, on the DeepEncoder global-attention workload (B=1, 12 heads,
-64x64 grid, D=64, bf16), inputs resident in HBM.  Prints ONE JSON line.
+64x64 grid, D=64, bf16), inputs resident in HBM.  The fused call
+relpos_attn_fused (the same step in one launch, bias computed in the attention
+kernel) is timed beside it.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload deepencoder]
 """
@@ -193,6 +195,14 @@ def main():
         build()
         attn()
 
+    out_fused = torch.empty_like(out)
+    ws_fused = torch.empty(rp.fused_workspace_bytes(w.B, w.heads, H, W, q.dtype,
+                                                    torch.cuda.get_device_properties(dev).multi_processor_count),
+                           dtype=torch.uint8, device=dev)
+
+    def fused():
+        rp.relpos_attn_fused(q, k, v, th, tw, H, W, scale, out=out_fused, workspace=ws_fused)
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -203,6 +213,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
+        fused()
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
 
@@ -229,11 +240,13 @@ def main():
 
     attn_ms = time_loop(attn, args.steps)
     build_ms = time_loop(build, args.steps)
+    fused_ms = time_loop(fused, args.steps)
     mem_after = torch.cuda.memory_allocated()
 
     # Output check on sampled rows of the last call (two heads) against the oracle
     # is left to the test-suite; here only finiteness is asserted.
     finite = bool(torch.isfinite(out).all().item())
+    fused_diff = (out_fused - out).abs().max().item()
 
     flops = w.flops
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -278,6 +291,14 @@ def main():
             "frac": round(attn_tflops / PEAK_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": attn_bytes,
+        },
+        "fused": {
+            "call": "relpos_attn_fused (bias rows computed in the attention kernel; no rel_h/rel_w tensors)",
+            "ms_per_call": round(fused_ms, 5),
+            "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+            "pct_bf16_peak": round(100.0 * flops / (fused_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+            "workspace_bytes": ws_fused.numel(),
+            "max_abs_diff_vs_step": fused_diff,
         },
         "output_finite": finite,
         "allocated_delta_bytes": mem_after - mem_before,

@@ -142,10 +142,11 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
  * faster): a grid of one 8-wave workgroup per compute unit (P of them) over
  * units of 256 consecutive queries of one (b, h), T key tiles each.  The
  * first floor(units / P) * P units run whole, one round at a time; the rest
- * of the last round are cut at key tile s = T*k/(k+1) (k = ceil(rest /
- * (P - rest))): their heads [0, s) run on `rest` workgroups and their tails
- * [s, T) on the others, k per workgroup, so every workgroup of the last
- * round has about s tiles.  Heads and tails store their unnormalised
+ * of the last round are cut at key tile s = (T*k + 6*(k-1))/(k+1) (k =
+ * ceil(rest / (P - rest)), rounded to nearest): their heads [0, s) run on
+ * `rest` workgroups and their tails [s, T) on the others, k per workgroup;
+ * s balances s + 6 against k*(T - s + 6), 6 tiles being the measured fixed
+ * cost of one segment.  Heads and tails store their unnormalised
  * output, reference maximum and row sum in the workspace, and a second
  * kernel on the same stream merges each unit's head and tail (in that order)
  * and writes its output.  Results are bitwise reproducible run to run, and
@@ -183,7 +184,9 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  * queries from q and the tables on MFMA (fp32 accumulation, as relpos_build),
  * keeps them in its slot of the workspace and reads them back per key tile.
  * The launch is the persistent split launch of relpos_attn_fwd_ws (one 8-wave
- * workgroup per compute unit, last round split, merge kernel when split).
+ * workgroup per compute unit, merge kernel when split) with a fixed cost of
+ * 12 tiles per segment in place of 6; the last round is left whole when its
+ * split would not be faster (max(s + 12, k*(T - s + 12)) + 4 >= T + 12).
  *
  * Arguments: q, k, v, out, B, heads, H, W, D, scale, in_dtype, out_dtype and
  * stream as for relpos_attn_fwd, plus
@@ -237,7 +240,7 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  * both measured); configuration 1 counts a last round with at most one
  * workgroup per compute unit at 0.77 (a lone workgroup runs one wave per
  * SIMD, measured faster per tile); configuration 5 costs the 8-wave factor
- * times (full rounds + (max(s, k*(T - s)) + 4) / T) in the terms of
+ * times (full rounds + (max(s + 6, k*(T - s + 6)) + 4) / T) in the terms of
  * relpos_attn_fwd_ws, and is considered only with a workspace, a last round
  * to split and k <= 4.  Ties go to the lower
  * number.  Inside the calls the environment variable RELPOS_ATTN_CFG=<0..5>

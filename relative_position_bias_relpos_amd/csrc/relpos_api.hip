@@ -112,7 +112,6 @@ int device_props(DeviceProps* out) {
 // compute units: 0 (8-wave workgroups), 1 (4-wave) or, when a workspace is
 // available, kAttnSplitConfig.  The cost model is the one documented with
 // relpos_attn_config in include/relpos.h; times are in 4-wave rounds.
-constexpr int kMergeTiles = 4;  // cost of the merge launch, in tile steps
 int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool allow_split) {
   const int64_t N = H * W;
   const int64_t T = ((H + 3) / 4) * ((W + 15) / 16);  // key tiles per query unit
@@ -127,14 +126,16 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
   const double t4 = static_cast<double>(full) + (rem == 0 ? 0.0 : (rem <= cus ? 0.77 : 1.0));
   int best = t8 <= t4 ? 0 : 1;
   // Split: the full rounds of 8-wave units, then a last round whose heads
-  // and tails (k per idle CU) take max(s, k*(T - s)) tiles, plus the merge;
-  // considered when at most 4 tails share a CU (a gain of 20% or more of the
-  // last round).
+  // and tails (k per idle CU) take max(s + F, k*(T - s + F)) tiles with F =
+  // kSplitSegmentTiles per segment, plus the merge; considered when at most 4
+  // tails share a CU.
   if (allow_split) {
-    const relpos::SplitPlan sp = relpos::split_plan(g8, static_cast<int>(T), cus);
+    constexpr int F = relpos::kSplitSegmentTiles;
+    const relpos::SplitPlan sp = relpos::split_plan(g8, static_cast<int>(T), cus, F);
     if (sp.rest > 0 && sp.s < T && sp.k <= 4) {
-      const int64_t last = sp.s > sp.k * (T - sp.s) ? sp.s : sp.k * (T - sp.s);
-      const double ts = a8 * (sp.rounds + static_cast<double>(last + kMergeTiles) / static_cast<double>(T));
+      const int64_t head = sp.s + F, tails = static_cast<int64_t>(sp.k) * (T - sp.s + F);
+      const int64_t last = head > tails ? head : tails;
+      const double ts = a8 * (sp.rounds + static_cast<double>(last + relpos::kMergeTiles) / static_cast<double>(T));
       if (ts < (best == 0 ? t8 : t4)) best = relpos::kAttnSplitConfig;
     }
   }

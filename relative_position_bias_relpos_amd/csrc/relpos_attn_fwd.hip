@@ -45,6 +45,7 @@
 //     rescaled by exp2(m_old - m_new), and the tile's p are recomputed.  Between
 //     such events no rescale of O is needed; p stays <= 2^15 (finite in fp16)
 //     and the row's first maximum keeps l >= 1.
+#include <algorithm>
 #include <type_traits>
 
 #include "relpos_attn_common.hpp"
@@ -90,15 +91,20 @@ __device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* 
     const int d = static_cast<int>((static_cast<float>(t) + 0.5f) * rcp_w);
     xa[i] = (AXIS_W ? t - d * W : qh0 + d) + L - 1;
   }
-  for (int rb = r_lo; rb <= r_hi; rb += 32) {
+  auto load_rows = [&](int rb, u32x4 (&tf)[4]) {
     const int r = rb + (lane & 31);
     const bool ok = r <= 2 * L - 2;
-    u32x4 tf[4];
 #pragma unroll
     for (int kd = 0; kd < 4; ++kd) {
       tf[kd] = ok ? *reinterpret_cast<const u32x4*>(tab + static_cast<size_t>(r) * kD + 16 * kd + 8 * half)
                   : u32x4{0, 0, 0, 0};
     }
+  };
+  u32x4 tf[4], tn[4];
+  load_rows(r_lo, tf);
+  for (int rb = r_lo; rb <= r_hi; rb += 32) {
+    const int r = rb + (lane & 31);
+    if (rb + 32 <= r_hi) load_rows(rb + 32, tn);  // the next block's rows load under this block's work
     f32x16 c = {};
 #pragma unroll
     for (int kd = 0; kd < 4; ++kd) c = mfma32<BF16>(qf[kd], tf[kd], c);
@@ -109,18 +115,22 @@ __device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* 
       const int off = static_cast<unsigned>(x) < static_cast<unsigned>(L) ? 4 * (row * Ls + x) : kOob;
       __builtin_amdgcn_raw_buffer_store_b32(as_uint(c[i]), rs, off, 0, 0);
     }
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) tf[kd] = tn[kd];
   }
 }
 
 // rel_h and rel_w rows of the wave's 32 queries gq0 .. gq0+31 (clamped to the
 // last query, so rows of queries past the grid hold finite copies), written to
-// sh[j][0..H) and sw[j][0..W) with row strides Hs >= H and Ws >= W; the columns
-// [H, Hs) and [W, Ws) are set to -inf (keys outside the grid).  gq0 is
-// wave-uniform.
+// sh[j][0..H) and sw[j][kw_lo..W) with row strides Hs >= H and Ws >= W; the
+// columns [H, Hs) and [W, Ws) are set to -inf (keys outside the grid).  rel_w
+// columns below kw_lo (key columns a segment starting past them never visits)
+// are left unwritten.  gq0 is wave-uniform.
 template <bool BF16>
 __device__ __forceinline__ void fused_bias_rows(const u32x4 (&qf)[4], const uint16_t* __restrict__ th,
                                                 const uint16_t* __restrict__ tw, float* sh, float* sw,
-                                                int H, int W, int Hs, int Ws, int gq0, int N, int lane) {
+                                                int H, int W, int Hs, int Ws, int gq0, int N, int kw_lo,
+                                                int lane) {
   const int half = lane >> 5;
   const int ga = gq0 < N - 1 ? gq0 : N - 1;
   const int gb = gq0 + 31 < N - 1 ? gq0 + 31 : N - 1;
@@ -128,8 +138,9 @@ __device__ __forceinline__ void fused_bias_rows(const u32x4 (&qf)[4], const uint
   const int qh1 = gb / W, qw1 = gb - qh1 * W;
   const float rcp_w = 1.0f / static_cast<float>(W);
   bias_axis<BF16, false>(qf, th, H, qh0, qw0, gb - ga, W, rcp_w, qh0, qh1 + H - 1, sh, Hs, lane);
-  // A wave that wraps to a new grid row holds every qw.
-  const int rw_lo = qh0 == qh1 ? qw0 : 0, rw_hi = qh0 == qh1 ? qw1 + W - 1 : 2 * W - 2;
+  // A wave that wraps to a new grid row holds every qw.  Columns x >= kw_lo
+  // need table rows r = qw + W - 1 - x <= max qw + W - 1 - kw_lo.
+  const int rw_lo = qh0 == qh1 ? qw0 : 0, rw_hi = (qh0 == qh1 ? qw1 : W - 1) + W - 1 - kw_lo;
   bias_axis<BF16, true>(qf, tw, W, qh0, qw0, gb - ga, W, rcp_w, rw_lo, rw_hi, sw, Ws, lane);
   const int j = lane & 31;
   for (int p = H + half; p < Hs; p += 2) sh[j * Hs + p] = -__builtin_inff();
@@ -359,12 +370,12 @@ __device__ __forceinline__ void attn_segment(
   const TilePos p1 = next_tile(p0, H);
   const TilePos p2 = next_tile(p1, H);
   if constexpr (FUSED) {
+    load_tile(p0);
     // This wave's 32 bias rows; the wave reads back only its own rows, so
     // waiting for its stores (vmcnt also counts stores) is enough.
     const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar addresses
     fused_bias_rows<BF16>(qf, th, tw, bias_slot + wu * 32 * hs, bias_slot + BM * hs + wu * 32 * wst,
-                          H, W, hs, wst, q0 + wu * 32, N, lane);
-    load_tile(p0);
+                          H, W, hs, wst, q0 + wu * 32, N, p0.kw, lane);
     store_tile(0);
     load_tile(p1);
     store_tile(1);
@@ -691,7 +702,14 @@ hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
   SplitPlan plan{};
   if constexpr (SPLIT) {
     ws = static_cast<float*>(a.ws);
-    plan = split_plan(units, static_cast<int>(T), a.split_ctas);
+    const int pro = FUSED ? kFusedPrologueTiles : kSplitSegmentTiles;
+    plan = split_plan(units, static_cast<int>(T), a.split_ctas, pro);
+    if (FUSED && plan.rest > 0 && plan.s < T) {
+      // The fused launch has no unsplit alternative: keep the last round
+      // whole when its split would not be faster (many tails per CU).
+      const int64_t last = std::max<int64_t>(plan.s + pro, static_cast<int64_t>(plan.k) * (T - plan.s + pro));
+      if (last + kMergeTiles >= T + pro) plan.s = static_cast<int>(T);
+    }
     grid = static_cast<unsigned>(a.split_ctas);
   }
   const float c2 = a.scale * kLog2e;

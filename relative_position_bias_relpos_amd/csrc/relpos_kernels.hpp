@@ -51,6 +51,14 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 //   5: configuration 0 with the key range split over a persistent grid of
 //      split_ctas workgroups (needs the workspace)
 constexpr int kAttnSplitConfig = 5;
+// Fixed cost of one segment of the split launch (pipeline start and drain,
+// the piece store, cold K/V tiles at the cut), in key-tile steps, and the
+// same for the fused launch, whose segments also compute their bias rows.
+// Set by measurement: on the 64x64, 12-head workload (T = 64, k = 3) these
+// put the cut at s = 51 and s = 54, the fastest of a sweep of s.
+constexpr int kSplitSegmentTiles = 6;
+constexpr int kMergeTiles = 4;  // cost of the merge launch, in tile steps
+constexpr int kFusedPrologueTiles = 12;
 
 // Last-round split of configuration kAttnSplitConfig.  With `units` query
 // units of T key tiles on P workgroups (one per CU), `rounds` = units / P full
@@ -59,17 +67,20 @@ constexpr int kAttnSplitConfig = 5;
 // [s, T) on the idle ones, k tails each, every head and every tail starting
 // at the same tile so a head's K/V tiles are shared in L2.  s = T*k/(k+1)
 // balances the two (k = ceil(rest / (P - rest))).  s == T means no tails
-// (T < 2): the last round then runs unsplit too.
+// (T < 2): the last round then runs unsplit too.  With a fixed cost of `pro`
+// tiles per segment, s = (T*k + (k-1)*pro) / (k+1) balances s + pro against
+// k*(T - s + pro).
 struct SplitPlan {
   int rounds, rest, k, s;
 };
-inline SplitPlan split_plan(int64_t units, int T, int P) {
+inline SplitPlan split_plan(int64_t units, int T, int P, int pro = 0) {
   SplitPlan p{};
   p.rounds = static_cast<int>(units / P);
   p.rest = static_cast<int>(units - static_cast<int64_t>(p.rounds) * P);
   if (p.rest == 0) return p;
   p.k = (p.rest + (P - p.rest) - 1) / (P - p.rest);
-  p.s = static_cast<int>((static_cast<int64_t>(T) * p.k + (p.k + 1) / 2) / (p.k + 1));
+  p.s = static_cast<int>((static_cast<int64_t>(T) * p.k + static_cast<int64_t>(p.k - 1) * pro + (p.k + 1) / 2) /
+                         (p.k + 1));
   if (p.s < 1) p.s = 1;
   if (p.s > T - 1) p.s = T < 2 ? T : T - 1;
   return p;

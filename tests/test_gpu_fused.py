@@ -167,3 +167,28 @@ def test_no_allocation_during_calls():
     assert torch.cuda.memory_allocated() == before
     assert torch.cuda.max_memory_allocated() == before
     assert abs(free_before - free_after) < 2 * 1024 * 1024
+
+
+def test_last_round_with_one_idle_cu():
+    """units = CUs - 1: splitting would put every tail on the one idle CU, so
+    the fused launch keeps the last round whole.  Parity, and a time of the
+    order of one unit's work (not one tail per unit in a row)."""
+    cus = _cus()
+    d = G.make("tiny", B=1, heads=cus - 1, H=16, W=16)
+    ref, _, _ = G.oracle_full(d)
+    _check(f"{cus - 1} units", np.abs(G.f64(_fused(d)) - ref))
+    g = G.to_dev(d)
+    ws = torch.empty(_ws_bytes(16, 16), dtype=torch.uint8, device="cuda")
+    call = lambda: rp.relpos_attn_fused(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], 16, 16,
+                                        d["scale"], workspace=ws)
+    call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    print(f"[fused] {cus - 1} units of 4 tiles: {ms * 1e3:.1f} us", flush=True)
+    assert ms < 1.0
