@@ -6,7 +6,7 @@ relpos_attn_fwd, on the DeepEncoder global-attention workload (B=1, 12 heads,
 relpos_attn_fused (the same step in one launch, bias computed in the attention
 kernel) is timed beside it.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload deepencoder]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 200] [--workload deepencoder]
 """
 
 import argparse
@@ -149,7 +149,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the GPU clock needs about 20 ms of work to settle")
     ap.add_argument("--workload", default="deepencoder")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -57,6 +57,21 @@ namespace {
 
 using namespace attn;
 
+// LDS row of a V tile.  8-wave workgroups (one per CU) use 96 halves (48
+// dwords): the four rows a 16-lane group of the transpose read touches then
+// start 0, 16, 32 and 48 banks apart and two such groups (32 lanes) cover the
+// 64 banks once; with K's 72 halves the second group's rows fall on the first
+// group's banks.  Smaller workgroups keep 72 halves so that two of them still
+// fit a CU's LDS.
+template <int NW>
+constexpr int v_stride() {
+  return NW >= 8 ? 96 : kKStride;
+}
+template <int NW>
+constexpr size_t attn32_lds_bytes() {
+  return kSlots * static_cast<size_t>(kTileKeys) * (kKStride + v_stride<NW>()) * 2;
+}
+
 // ---- bias computed in the attention kernel ----------------------------------
 // One axis of the bias for the 32 queries of a wave: out[j][x] = q_j . T[a_j + L
 // - 1 - x] for x in [0, L), with a_j the query's coordinate along the axis
@@ -176,11 +191,13 @@ __device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw, float* bias_slot) {
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
+  constexpr int kVStride = v_stride<NW>();
+  constexpr int kVTileHalves = kTileKeys * kVStride;
   const int N = H * W;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [kSlots][64][kKStride]
-  uint16_t* Vs = Ks + kSlots * kTileHalves;          // [kSlots][64][kKStride]
+  uint16_t* Vs = Ks + kSlots * kTileHalves;          // [kSlots][64][kVStride]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,7 +223,7 @@ __device__ __forceinline__ void attn_segment(
   // ---- K/V tile staging: global -> registers -> LDS (row-major, 16 B chunks)
   constexpr int CH = (kTileKeys * kD / 8) / NT;  // 16-byte chunks of K (and of V) per thread
   static_assert(CH >= 1, "workgroup too large for one tile");
-  int ch_r[CH], ch_c[CH], ch_voff[CH], ch_lds[CH];
+  int ch_r[CH], ch_c[CH], ch_voff[CH], ch_lds[CH], ch_vlds[CH];
 #pragma unroll
   for (int s = 0; s < CH; ++s) {
     const int cid = tid + s * NT;
@@ -215,6 +232,7 @@ __device__ __forceinline__ void attn_segment(
     ch_c[s] = o & 15;
     ch_voff[s] = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * dc;  // bytes from the tile origin
     ch_lds[s] = o * kKStride + 8 * dc;
+    ch_vlds[s] = o * kVStride + 8 * dc;
   }
   u32x4 kreg[CH], vreg[CH];
   const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
@@ -245,7 +263,7 @@ __device__ __forceinline__ void attn_segment(
   };
   auto store_tile = [&](int slot) {
     uint16_t* kb = Ks + slot * kTileHalves;
-    uint16_t* vb = Vs + slot * kTileHalves;
+    uint16_t* vb = Vs + slot * kVTileHalves;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
       *reinterpret_cast<u32x4*>(kb + ch_lds[s]) = kreg[s];
@@ -254,7 +272,7 @@ __device__ __forceinline__ void attn_segment(
 #pragma unroll
         for (int w = 0; w < 4; ++w) x[w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
       }
-      *reinterpret_cast<u32x4*>(vb + ch_lds[s]) = x;
+      *reinterpret_cast<u32x4*>(vb + ch_vlds[s]) = x;
     }
   };
 
@@ -349,14 +367,14 @@ __device__ __forceinline__ void attn_segment(
   f32x16 acc[2];
   // O^T += V^T P^T for the tile in `slot`: four 16-key steps, two 32-row d tiles.
   auto pv = [&](int slot, const u32x4 (&pf)[4]) {
-    const uint16_t* vb = Vs + slot * kTileHalves;
+    const uint16_t* vb = Vs + slot * kVTileHalves;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
+        const uint16_t* vp = vb + (16 * ks + tr_row) * kVStride + 32 * dt + tr_col;
         const u32x2 lo = ds_read_tr16(vp);
-        const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
+        const u32x2 hi = ds_read_tr16(vp + 8 * kVStride);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
         acc[dt] = mfma32<false>(vf, pf[ks], acc[dt]);
       }
@@ -421,16 +439,16 @@ __device__ __forceinline__ void attn_segment(
     // Operands of this step's MFMAs: K^T fragments of tile t+1 and V^T
     // fragments of tile t-1, read from LDS two chunks ahead of their use.
     const uint16_t* kb = Ks + ((t + 1) & (kSlots - 1)) * kTileHalves;
-    const uint16_t* vb = Vs + ((t - 1) & (kSlots - 1)) * kTileHalves;
+    const uint16_t* vb = Vs + ((t - 1) & (kSlots - 1)) * kVTileHalves;
     auto read_k = [&](int i) -> u32x4 {
       const int st = i & 1, kd = i >> 1;
       return *reinterpret_cast<const u32x4*>(kb + (32 * st + (lane & 31)) * kKStride + 16 * kd + 8 * half);
     };
     auto read_v = [&](int i) -> u32x4 {
       const int dt = i & 1, ks = i >> 1;
-      const uint16_t* vp = vb + (16 * ks + tr_row) * kKStride + 32 * dt + tr_col;
+      const uint16_t* vp = vb + (16 * ks + tr_row) * kVStride + 32 * dt + tr_col;
       const u32x2 lo = ds_read_tr16(vp);
-      const u32x2 hi = ds_read_tr16(vp + 8 * kKStride);
+      const u32x2 hi = ds_read_tr16(vp + 8 * kVStride);
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     u32x4 kf[8], vf[8];
@@ -688,7 +706,8 @@ int64_t split_piece_bytes(int ctas) {
 }
 
 template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED = false>
-hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
+hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
+  constexpr size_t lds = attn32_lds_bytes<NW>();
   auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT, FUSED>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -731,24 +750,24 @@ hipError_t launch_cfg(const AttnArgs& a, size_t lds, hipStream_t stream) {
 }
 
 template <bool BF16, bool OUT_F32, int NW, bool SPLIT, bool FUSED = false>
-hipError_t launch_nw(const AttnArgs& a, size_t lds, hipStream_t stream) {
+hipError_t launch_nw(const AttnArgs& a, hipStream_t stream) {
   // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED>(a, lds, stream)
-                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED>(a, lds, stream);
+  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED>(a, stream)
+                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED>(a, stream);
 }
 
 template <bool BF16, bool OUT_F32>
-hipError_t launch_dt(const AttnArgs& a, int cfg, size_t lds, hipStream_t stream) {
+hipError_t launch_dt(const AttnArgs& a, int cfg, hipStream_t stream) {
   switch (cfg) {
-    case 0: return launch_nw<BF16, OUT_F32, 8, false>(a, lds, stream);
-    case 1: return launch_nw<BF16, OUT_F32, 4, false>(a, lds, stream);
-    case 2: return launch_nw<BF16, OUT_F32, 2, false>(a, lds, stream);
-    default: return launch_nw<BF16, OUT_F32, 8, true>(a, lds, stream);  // kAttnSplitConfig
+    case 0: return launch_nw<BF16, OUT_F32, 8, false>(a, stream);
+    case 1: return launch_nw<BF16, OUT_F32, 4, false>(a, stream);
+    case 2: return launch_nw<BF16, OUT_F32, 2, false>(a, stream);
+    default: return launch_nw<BF16, OUT_F32, 8, true>(a, stream);  // kAttnSplitConfig
   }
 }
 
-size_t attn32_lds_bytes() { return 2 * kSlots * static_cast<size_t>(kTileHalves) * 2; }
+
 
 }  // namespace
 
@@ -766,28 +785,32 @@ size_t attn_fused_workspace_bytes(int H, int W, int ctas) {
 }
 
 hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = attn32_lds_bytes();
   if (a.bf16) {
-    return a.out_f32 ? launch_nw<true, true, 8, true, true>(a, lds, stream)
-                     : launch_nw<true, false, 8, true, true>(a, lds, stream);
+    return a.out_f32 ? launch_nw<true, true, 8, true, true>(a, stream)
+                     : launch_nw<true, false, 8, true, true>(a, stream);
   }
-  return a.out_f32 ? launch_nw<false, true, 8, true, true>(a, lds, stream)
-                   : launch_nw<false, false, 8, true, true>(a, lds, stream);
+  return a.out_f32 ? launch_nw<false, true, 8, true, true>(a, stream)
+                   : launch_nw<false, false, 8, true, true>(a, stream);
 }
 
 size_t attn_lds_bytes(int cfg, int H, int W) {
   (void)H;
   (void)W;
-  return cfg == 3 || cfg == 4 ? attn16_lds_bytes() : attn32_lds_bytes();
+  switch (cfg) {
+    case 1: return attn32_lds_bytes<4>();
+    case 2: return attn32_lds_bytes<2>();
+    case 3:
+    case 4: return attn16_lds_bytes();
+    default: return attn32_lds_bytes<8>();  // 0 and kAttnSplitConfig
+  }
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
   if (cfg == 3 || cfg == 4) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
-  const size_t lds = attn32_lds_bytes();
   if (a.bf16) {
-    return a.out_f32 ? launch_dt<true, true>(a, cfg, lds, stream) : launch_dt<true, false>(a, cfg, lds, stream);
+    return a.out_f32 ? launch_dt<true, true>(a, cfg, stream) : launch_dt<true, false>(a, cfg, stream);
   }
-  return a.out_f32 ? launch_dt<false, true>(a, cfg, lds, stream) : launch_dt<false, false>(a, cfg, lds, stream);
+  return a.out_f32 ? launch_dt<false, true>(a, cfg, stream) : launch_dt<false, false>(a, cfg, stream);
 }
 
 }  // namespace relpos
