@@ -12,8 +12,9 @@ order, q, k, v (shape ``[B, heads, H*W, D]``) and the two tables rel_pos_h
 workload dtype (round-to-nearest-even, torch ``.to``).
 
 The workloads stand in for DeepEncoder's global attention (the PR #55629 page's
-64x64 case) and variants of it; trained tables and real activations are not
-available, so normal/uniform draws of the stated spread replace them.
+64x64 case), variants of it and its windowed blocks cut into 14x14 windows;
+trained tables and real activations are not available, so normal/uniform draws
+of the stated spread replace them.
 """
 
 from dataclasses import dataclass, replace
@@ -59,6 +60,11 @@ WORKLOADS = {
                              qk_mul=4.0, v_dist="uniform", table_std=0.1),
     "rect": Workload("rect", B=2, heads=12, H=48, W=80),
     "vitl": Workload("vitl", B=2, heads=16, H=96, W=96, build_in_step=True),
+    # Windowed blocks: the 64x64 grid padded to 70x70 and cut into 25 windows of
+    # 14x14, each an independent grid with its own 27-row tables; B counts the
+    # windows of one image.  The window size is not on the PR #55629 page (its
+    # windowed blocks stay on SDPA); 14 is a stand-in.
+    "windowed": Workload("windowed", B=25, heads=12, H=14, W=14),
 }
 
 # Grids whose token count is not a multiple of any tile size: correctness only.
