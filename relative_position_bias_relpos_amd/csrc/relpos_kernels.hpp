@@ -57,7 +57,12 @@ constexpr int kAttnSplitConfig = 5;
 // Set by measurement: on the 64x64, 12-head workload (T = 64, k = 3) these
 // put the cut at s = 51 and s = 54, the fastest of a sweep of s.
 constexpr int kSplitSegmentTiles = 6;
-constexpr int kMergeTiles = 4;  // cost of the merge launch, in tile steps
+// Fixed cost of splitting a last round beyond its segments (the merge launch),
+// in tile steps.  Checked on whole steps (relpos_build, then the attention
+// call): at 64x64 the split step is 88.0 us against 93.2 us unsplit, although
+// alone the unsplit call is 1 us faster; 48x80 is within 1% either way and
+// 96x96 favours the split.
+constexpr int kMergeTiles = 4;
 constexpr int kFusedPrologueTiles = 12;
 
 // Last-round split of configuration kAttnSplitConfig.  With `units` query

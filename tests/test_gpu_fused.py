@@ -7,6 +7,8 @@ out), every output on small and ragged grids, sampled rows at full size.
 
 import ctypes
 
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -157,6 +159,7 @@ def test_no_allocation_during_calls():
                                         d["scale"], out=out, workspace=ws)
     call()
     torch.cuda.synchronize()
+    gc.collect()  # tensors of earlier tests must not be freed inside the measured loop
     torch.cuda.reset_peak_memory_stats()
     before = torch.cuda.memory_allocated()
     free_before, _ = torch.cuda.mem_get_info()
@@ -164,8 +167,8 @@ def test_no_allocation_during_calls():
         call()
     torch.cuda.synchronize()
     free_after, _ = torch.cuda.mem_get_info()
-    assert torch.cuda.memory_allocated() == before
-    assert torch.cuda.max_memory_allocated() == before
+    assert torch.cuda.memory_allocated() <= before
+    assert torch.cuda.max_memory_allocated() == before  # the peak never rose above the start
     assert abs(free_before - free_after) < 2 * 1024 * 1024
 
 
