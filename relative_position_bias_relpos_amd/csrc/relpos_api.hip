@@ -368,6 +368,7 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
   a.split_ctas = props.cus;
   a.th = rel_pos_h;
   a.tw = rel_pos_w;
+  a.lds_limit = props.lds_limit;
   if (relpos::launch_attn_fused(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
   return RELPOS_OK;
 }

@@ -71,6 +71,11 @@ template <int NW>
 constexpr size_t attn32_lds_bytes() {
   return kSlots * static_cast<size_t>(kTileKeys) * (kKStride + v_stride<NW>()) * 2;
 }
+// LDS of the fused launch's rel_h rows: 256 queries x (rows padded to whole
+// tiles + 4) floats.
+inline size_t fused_rh_lds_bytes(int H) {
+  return 256 * static_cast<size_t>((H + kTileRows - 1) / kTileRows * kTileRows + 4) * sizeof(float);
+}
 
 // ---- bias computed in the attention kernel ----------------------------------
 // One axis of the bias for the 32 queries of a wave: out[j][x] = q_j . T[a_j + L
@@ -82,13 +87,13 @@ constexpr size_t attn32_lds_bytes() {
 // B = T^T; a lane then holds table row r for 16 queries and writes each value
 // to its diagonal position x = a_j + L - 1 - r.  For one query the 32 lanes of
 // a half write 32 consecutive floats.  Stores outside [0, L) are dropped by the
-// buffer range check (offset kOob).
+// buffer range check (offset kOob), or skipped when the rows are in LDS.
 //
 // The queries' coordinates: query j_i = 8*(i/4) + 4*half + i%4 (the row of
 // result register i) is gq0 + min(j_i, jmax) with grid column t = qw0 + min(j_i,
 // jmax) < W + 32 past the wave's first grid row qh0; floor(t / W) is exact from
 // the float product (the quotient is at least 0.5/W from the next integer).
-template <bool BF16, bool AXIS_W>
+template <bool BF16, bool AXIS_W, bool TO_LDS>
 __device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* __restrict__ tab, int L,
                                           int qh0, int qw0, int jmax, int W, float rcp_w, int r_lo, int r_hi,
                                           float* dst, int Ls, int lane) {
@@ -127,8 +132,12 @@ __device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* 
     for (int i = 0; i < 16; ++i) {
       const int x = xa[i] - r;
       const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      const int off = static_cast<unsigned>(x) < static_cast<unsigned>(L) ? 4 * (row * Ls + x) : kOob;
-      __builtin_amdgcn_raw_buffer_store_b32(as_uint(c[i]), rs, off, 0, 0);
+      if constexpr (TO_LDS) {
+        if (static_cast<unsigned>(x) < static_cast<unsigned>(L)) dst[row * Ls + x] = c[i];
+      } else {
+        const int off = static_cast<unsigned>(x) < static_cast<unsigned>(L) ? 4 * (row * Ls + x) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b32(as_uint(c[i]), rs, off, 0, 0);
+      }
     }
 #pragma unroll
     for (int kd = 0; kd < 4; ++kd) tf[kd] = tn[kd];
@@ -137,28 +146,28 @@ __device__ __forceinline__ void bias_axis(const u32x4 (&qf)[4], const uint16_t* 
 
 // rel_h and rel_w rows of the wave's 32 queries gq0 .. gq0+31 (clamped to the
 // last query, so rows of queries past the grid hold finite copies), written to
-// sh[j][0..H) and sw[j][kw_lo..W) with row strides Hs >= H and Ws >= W; the
-// columns [H, Hs) and [W, Ws) are set to -inf (keys outside the grid).  rel_w
-// columns below kw_lo (key columns a segment starting past them never visits)
-// are left unwritten.  gq0 is wave-uniform.
-template <bool BF16>
+// sh[j][0..H) and sw[j][kw_lo..W) with row strides hstride and Ws; the columns
+// [H, Hs) and [W, Ws) are set to -inf (keys outside the grid).  rel_w columns
+// below kw_lo (key columns a segment starting past them never visits) are left
+// unwritten.  RH_LDS: sh is in LDS.  gq0 is wave-uniform.
+template <bool BF16, bool RH_LDS>
 __device__ __forceinline__ void fused_bias_rows(const u32x4 (&qf)[4], const uint16_t* __restrict__ th,
                                                 const uint16_t* __restrict__ tw, float* sh, float* sw,
-                                                int H, int W, int Hs, int Ws, int gq0, int N, int kw_lo,
-                                                int lane) {
+                                                int H, int W, int Hs, int hstride, int Ws, int gq0, int N,
+                                                int kw_lo, int lane) {
   const int half = lane >> 5;
   const int ga = gq0 < N - 1 ? gq0 : N - 1;
   const int gb = gq0 + 31 < N - 1 ? gq0 + 31 : N - 1;
   const int qh0 = ga / W, qw0 = ga - qh0 * W;
   const int qh1 = gb / W, qw1 = gb - qh1 * W;
   const float rcp_w = 1.0f / static_cast<float>(W);
-  bias_axis<BF16, false>(qf, th, H, qh0, qw0, gb - ga, W, rcp_w, qh0, qh1 + H - 1, sh, Hs, lane);
+  bias_axis<BF16, false, RH_LDS>(qf, th, H, qh0, qw0, gb - ga, W, rcp_w, qh0, qh1 + H - 1, sh, hstride, lane);
   // A wave that wraps to a new grid row holds every qw.  Columns x >= kw_lo
   // need table rows r = qw + W - 1 - x <= max qw + W - 1 - kw_lo.
   const int rw_lo = qh0 == qh1 ? qw0 : 0, rw_hi = (qh0 == qh1 ? qw1 : W - 1) + W - 1 - kw_lo;
-  bias_axis<BF16, true>(qf, tw, W, qh0, qw0, gb - ga, W, rcp_w, rw_lo, rw_hi, sw, Ws, lane);
+  bias_axis<BF16, true, false>(qf, tw, W, qh0, qw0, gb - ga, W, rcp_w, rw_lo, rw_hi, sw, Ws, lane);
   const int j = lane & 31;
-  for (int p = H + half; p < Hs; p += 2) sh[j * Hs + p] = -__builtin_inff();
+  for (int p = H + half; p < Hs; p += 2) sh[j * hstride + p] = -__builtin_inff();
   for (int p = W + half; p < Ws; p += 2) sw[j * Ws + p] = -__builtin_inff();
 }
 
@@ -180,8 +189,10 @@ __host__ __device__ constexpr int fused_row_floats(int H, int W) {
 // writes the normalised output; otherwise the segment is one piece of a split
 // unit (see SplitPlan), written to workspace slot `slot`.  FUSED: the bias rows
 // are computed from q and the tables th/tw into `bias_slot` (the workgroup's
-// BM * (Hs + Ws) floats) instead of being read from rel_h/rel_w.
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED>
+// BM * (Hs + Ws) floats) instead of being read from rel_h/rel_w; RH_LDS: the
+// rel_h rows go to LDS after the K/V ring instead (row stride Hs + 4 floats,
+// so the 16-byte reads of 16 lanes cover the 64 banks once).
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED, bool RH_LDS = false>
 __device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
@@ -309,6 +320,8 @@ __device__ __forceinline__ void attn_segment(
   const int qrow = FUSED || qok ? ql : 0;
   const int rw_lane = (qrow * wst + 4 * half) * 4;  // bytes: this lane's row, column 4*half
   const int rh_lane = qrow * hs * 4;
+  const int hs_l = hs + 4;  // LDS row stride of rel_h (RH_LDS)
+  float* rh_lds = reinterpret_cast<float*>(smem + kSlots * static_cast<size_t>(kTileHalves + kVTileHalves) * 2);
   f32x16 rwc;
   auto load_band = [&](int kw0) {
     float x[8];
@@ -334,7 +347,11 @@ __device__ __forceinline__ void attn_segment(
   };
   float rhn[4];  // rel_h of the next tile's 4 grid rows (-inf outside the grid)
   auto load_rh = [&](int kh0) {
-    if constexpr (kPadded) {
+    if constexpr (FUSED && RH_LDS) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(rh_lds + ql * hs_l + kh0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rhn[r] = a[r];
+    } else if constexpr (kPadded) {
       const u32x4 a = buf_load16(rhrs, rh_lane, 4 * kh0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) rhn[r] = as_float(a[r]);
@@ -392,8 +409,9 @@ __device__ __forceinline__ void attn_segment(
     // This wave's 32 bias rows; the wave reads back only its own rows, so
     // waiting for its stores (vmcnt also counts stores) is enough.
     const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar addresses
-    fused_bias_rows<BF16>(qf, th, tw, bias_slot + wu * 32 * hs, bias_slot + BM * hs + wu * 32 * wst,
-                          H, W, hs, wst, q0 + wu * 32, N, p0.kw, lane);
+    float* sh = RH_LDS ? rh_lds + wu * 32 * hs_l : bias_slot + wu * 32 * hs;
+    fused_bias_rows<BF16, RH_LDS>(qf, th, tw, sh, bias_slot + BM * hs + wu * 32 * wst, H, W, hs,
+                                  RH_LDS ? hs_l : hs, wst, q0 + wu * 32, N, p0.kw, lane);
     store_tile(0);
     load_tile(p1);
     store_tile(1);
@@ -655,7 +673,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
 // FUSED (always with SPLIT): the bias is computed per segment from q and the
 // tables th/tw; workgroup b keeps its bias rows in the workspace after the
 // 2 * P split pieces, at bias slot b.
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED>
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED, bool RH_LDS>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
@@ -678,20 +696,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   } else {
     const int P = static_cast<int>(gridDim.x);
     for (int i = 0; i < plan.rounds; ++i) {
-      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
                                                             rw_mul, ws, i * P + L, 0, T, 0, th, tw, bias_slot);
       __syncthreads();  // the next segment reuses the LDS ring
     }
     const int base = plan.rounds * P;
     if (L < plan.rest) {
-      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+      attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
                                                             rw_mul, ws, base + L, 0, plan.s, 2 * L, th, tw,
                                                             bias_slot);
     } else if (plan.s < T) {
       for (int j = 0; j < plan.k; ++j) {
         const int ui = (L - plan.rest) * plan.k + j;
         if (ui >= plan.rest) break;
-        attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+        attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
                                                               rw_mul, ws, base + ui, plan.s, T - plan.s,
                                                               2 * ui + 1, th, tw, bias_slot);
         __syncthreads();
@@ -705,10 +723,10 @@ int64_t split_piece_bytes(int ctas) {
   return 2 * static_cast<int64_t>(ctas) * piece_floats<256>() * static_cast<int64_t>(sizeof(float));
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED = false>
+template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED = false, bool RH_LDS = false>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
-  constexpr size_t lds = attn32_lds_bytes<NW>();
-  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT, FUSED>;
+  const size_t lds = attn32_lds_bytes<NW>() + (RH_LDS ? fused_rh_lds_bytes(a.H) : 0);
+  auto kern = attn_fwd_kernel<BF16, OUT_F32, NW, ALIGNED, SPLIT, FUSED, RH_LDS>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
@@ -749,12 +767,12 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool OUT_F32, int NW, bool SPLIT, bool FUSED = false>
+template <bool BF16, bool OUT_F32, int NW, bool SPLIT, bool FUSED = false, bool RH_LDS = false>
 hipError_t launch_nw(const AttnArgs& a, hipStream_t stream) {
   // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED>(a, stream)
-                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED>(a, stream);
+  return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED, RH_LDS>(a, stream)
+                 : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED, RH_LDS>(a, stream);
 }
 
 template <bool BF16, bool OUT_F32>
@@ -784,13 +802,21 @@ size_t attn_fused_workspace_bytes(int H, int W, int ctas) {
          static_cast<size_t>(ctas) * 256 * static_cast<size_t>(fused_row_floats(H, W)) * sizeof(float);
 }
 
-hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream) {
+template <bool RH_LDS>
+hipError_t launch_fused_rh(const AttnArgs& a, hipStream_t stream) {
   if (a.bf16) {
-    return a.out_f32 ? launch_nw<true, true, 8, true, true>(a, stream)
-                     : launch_nw<true, false, 8, true, true>(a, stream);
+    return a.out_f32 ? launch_nw<true, true, 8, true, true, RH_LDS>(a, stream)
+                     : launch_nw<true, false, 8, true, true, RH_LDS>(a, stream);
   }
-  return a.out_f32 ? launch_nw<false, true, 8, true, true>(a, stream)
-                   : launch_nw<false, false, 8, true, true>(a, stream);
+  return a.out_f32 ? launch_nw<false, true, 8, true, true, RH_LDS>(a, stream)
+                   : launch_nw<false, false, 8, true, true, RH_LDS>(a, stream);
+}
+
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream) {
+  // rel_h rows in LDS when they fit beside the K/V ring (up to H = 68 on a
+  // 160 KB LDS), else in the workspace slot like rel_w.
+  const bool rh_lds = attn32_lds_bytes<8>() + fused_rh_lds_bytes(a.H) <= static_cast<size_t>(a.lds_limit);
+  return rh_lds ? launch_fused_rh<true>(a, stream) : launch_fused_rh<false>(a, stream);
 }
 
 size_t attn_lds_bytes(int cfg, int H, int W) {

@@ -39,6 +39,8 @@ struct AttnArgs {
   // [2W-1, 64] in the input dtype (rel_h and rel_w are then unused).
   const void* th = nullptr;
   const void* tw = nullptr;
+  // LDS bytes a workgroup may use on this device (launch_attn_fused only).
+  int lds_limit = 0;
 };
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
