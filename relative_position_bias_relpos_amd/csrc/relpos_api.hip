@@ -221,6 +221,7 @@ relpos_status attn_fwd_impl(const void* q, const void* k, const void* v,
   relpos::AttnArgs a{q, k, v, rel_h, rel_w, out,
                      static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
                      bf16, out_dtype == RELPOS_FP32};
+  a.lds_limit = props.lds_limit;
   if (cfg == relpos::kAttnSplitConfig) {
     a.ws = workspace;
     a.split_ctas = props.cus;

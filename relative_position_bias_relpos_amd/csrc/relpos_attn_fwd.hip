@@ -189,9 +189,11 @@ __host__ __device__ constexpr int fused_row_floats(int H, int W) {
 // writes the normalised output; otherwise the segment is one piece of a split
 // unit (see SplitPlan), written to workspace slot `slot`.  FUSED: the bias rows
 // are computed from q and the tables th/tw into `bias_slot` (the workgroup's
-// BM * (Hs + Ws) floats) instead of being read from rel_h/rel_w; RH_LDS: the
-// rel_h rows go to LDS after the K/V ring instead (row stride Hs + 4 floats,
-// so the 16-byte reads of 16 lanes cover the 64 banks once).
+// BM * (Hs + Ws) floats) instead of being read from rel_h/rel_w.  RH_LDS: the
+// unit's rel_h rows live in LDS after the K/V ring (row stride Hs + 4 floats,
+// so the 16-byte reads of 16 lanes cover the 64 banks once): computed there
+// when FUSED, else copied there from rel_h once per segment (tile-aligned
+// grids only, whose rows are 16-byte aligned).
 template <bool BF16, bool OUT_F32, int NW, bool ALIGNED, bool SPLIT, bool FUSED, bool RH_LDS = false>
 __device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -347,7 +349,7 @@ __device__ __forceinline__ void attn_segment(
   };
   float rhn[4];  // rel_h of the next tile's 4 grid rows (-inf outside the grid)
   auto load_rh = [&](int kh0) {
-    if constexpr (FUSED && RH_LDS) {
+    if constexpr (RH_LDS) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(rh_lds + ql * hs_l + kh0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) rhn[r] = a[r];
@@ -404,6 +406,27 @@ __device__ __forceinline__ void attn_segment(
   const TilePos p0{(t0 % band_tiles) * kTileRows, (t0 / band_tiles) * kTileCols};
   const TilePos p1 = next_tile(p0, H);
   const TilePos p2 = next_tile(p1, H);
+  if constexpr (!FUSED && RH_LDS) {
+    static_assert(ALIGNED, "rel_h rows are copied in 16-byte chunks");
+    // This wave's 32 rel_h rows: H/4 chunks of 16 bytes per row, 64/(H/4)
+    // rows per pass; rows past the grid read zeros (their outputs are not
+    // written).  The wave reads back only its own rows.
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int row0 = q0 + wu * 32;
+    const int nrows = N - row0 < 32 ? (N - row0 > 0 ? N - row0 : 0) : 32;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(rel_h + (head + (row0 < N ? row0 : 0)) * H, static_cast<uint32_t>(nrows * H) * 4);
+    const int cpr = H / 4;
+    const int rpi = 64 / cpr;
+    const int lrow = lane / cpr, lcol = lane - lrow * cpr;
+    for (int r0 = 0; r0 < 32; r0 += rpi) {
+      const int row = r0 + lrow;
+      if (lrow < rpi && row < 32) {
+        const u32x4 x = buf_load16(rs, (row * H + 4 * lcol) * 4);
+        *reinterpret_cast<u32x4*>(rh_lds + (wu * 32 + row) * hs_l + 4 * lcol) = x;
+      }
+    }
+  }
   if constexpr (FUSED) {
     load_tile(p0);
     // This wave's 32 bias rows; the wave reads back only its own rows, so
@@ -691,7 +714,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     bias_slot = ws + 2 * static_cast<int64_t>(gridDim.x) * piece_floats<BM>() + blockIdx.x * slot_floats;
   }
   if constexpr (!SPLIT) {
-    attn_segment<BF16, OUT_F32, NW, ALIGNED, false, false>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
+    attn_segment<BF16, OUT_F32, NW, ALIGNED, false, false, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
                                                            rw_mul, ws, L, 0, T, 0, th, tw, bias_slot);
   } else {
     const int P = static_cast<int>(gridDim.x);
@@ -771,6 +794,12 @@ template <bool BF16, bool OUT_F32, int NW, bool SPLIT, bool FUSED = false, bool 
 hipError_t launch_nw(const AttnArgs& a, hipStream_t stream) {
   // Grids whose sides are multiples of the 4 x 16 key tile need no masking.
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
+  if constexpr (NW == 8 && !FUSED) {
+    // rel_h rows in LDS when they fit beside the ring (one workgroup per CU).
+    if (aligned && attn32_lds_bytes<8>() + fused_rh_lds_bytes(a.H) <= static_cast<size_t>(a.lds_limit)) {
+      return launch_cfg<BF16, OUT_F32, NW, true, SPLIT, false, true>(a, stream);
+    }
+  }
   return aligned ? launch_cfg<BF16, OUT_F32, NW, true, SPLIT, FUSED, RH_LDS>(a, stream)
                  : launch_cfg<BF16, OUT_F32, NW, false, SPLIT, FUSED, RH_LDS>(a, stream);
 }

@@ -39,7 +39,8 @@ struct AttnArgs {
   // [2W-1, 64] in the input dtype (rel_h and rel_w are then unused).
   const void* th = nullptr;
   const void* tw = nullptr;
-  // LDS bytes a workgroup may use on this device (launch_attn_fused only).
+  // LDS bytes a workgroup may use on this device (0: only the K/V ring is
+  // used; more lets 8-wave launches keep rel_h rows in LDS).
   int lds_limit = 0;
 };
 
