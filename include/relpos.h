@@ -181,8 +181,10 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  * Defines the same `out` as relpos_build + relpos_attn_fwd on the same inputs
  * (same tolerance against the definition; results differ from the two-call
  * path by rounding only).  Each workgroup computes the bias rows of its 256
- * queries from q and the tables on MFMA (fp32 accumulation, as relpos_build),
- * keeps them in its slot of the workspace and reads them back per key tile.
+ * queries from q and the tables on MFMA (fp32 accumulation, as relpos_build)
+ * and reads them back per key tile: rel_w rows from its slot of the
+ * workspace, rel_h rows from LDS when 256*(roundup(H,4)+4) floats fit beside
+ * the K/V staging (H <= 72 on a 160 KB LDS), else from the slot as well.
  * The launch is the persistent split launch of relpos_attn_fwd_ws (one 8-wave
  * workgroup per compute unit, merge kernel when split) with a fixed cost of
  * 12 tiles per segment in place of 6; the last round is left whole when its

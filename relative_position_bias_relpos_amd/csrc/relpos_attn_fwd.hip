@@ -6,9 +6,14 @@
 // Work layout
 //   * A unit is BM = 32*NW consecutive queries of one (batch, head); each of a
 //     workgroup's NW waves owns 32 of them.  Either one workgroup per unit
-//     takes all of the unit's key tiles, or (key-range split) a persistent
-//     grid of one workgroup per CU takes equal contiguous ranges of all
-//     (unit, tile) work, and units cut between ranges are merged afterwards.
+//     takes all of the unit's key tiles, or (key-range split, SplitPlan) a
+//     persistent grid of one workgroup per CU runs whole rounds of units and
+//     cuts the units of the last round at one key tile into a head and a
+//     tail on different workgroups, merged afterwards by split_merge_kernel.
+//   * Bias sources: the rel_h/rel_w tensors written by relpos_build (rel_h
+//     rows copied to LDS per segment when they fit beside the ring), or, in
+//     the fused launch, rows computed per segment from q and the tables
+//     (fused_bias_rows: rel_h to LDS when it fits, rel_w to a workspace slot).
 //   * Keys are visited in 2-D tiles of the key grid: 4 grid rows x 16 grid
 //     columns = 64 keys, in column bands (kw0 outer, kh0 inner).  Key o
 //     (0..63) of a tile is grid cell (kh0 + o/16, kw0 + o%16); cells outside

@@ -195,3 +195,14 @@ def test_last_round_with_one_idle_cu():
     ms = a.elapsed_time(b) / 5
     print(f"[fused] {cus - 1} units of 4 tiles: {ms * 1e3:.1f} us", flush=True)
     assert ms < 1.0
+
+
+@pytest.mark.parametrize("H,W", [(72, 16), (76, 16), (68, 32)])
+def test_rel_h_rows_at_the_lds_limit(H, W):
+    """H = 72 fills a 160 KB LDS exactly (rel_h rows in LDS), H = 76 does not
+    (rows in the workspace slot); both calls, every output."""
+    d = G.make("tiny", B=1, heads=2, H=H, W=W)
+    ref, _, _ = G.oracle_full(d)
+    _check(f"fused {H}x{W}", np.abs(G.f64(_fused(d)) - ref))
+    two, _, _ = G.gpu_run(d)
+    _check(f"two calls {H}x{W}", np.abs(G.f64(two) - ref))
