@@ -242,7 +242,8 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  * both measured); configuration 1 counts a last round with at most one
  * workgroup per compute unit at 0.77 (a lone workgroup runs one wave per
  * SIMD, measured faster per tile); configuration 5 costs the 8-wave factor
- * times (full rounds + (max(s + 6, k*(T - s + 6)) + 4) / T) in the terms of
+ * times 1.06 (the persistent grid's measured per-tile overhead) times (full
+ * rounds + (max(s + 6, k*(T - s + 6)) + 4) / T) in the terms of
  * relpos_attn_fwd_ws, and is considered only with a workspace, a last round
  * to split and k <= 4.  Ties go to the lower
  * number.  Inside the calls the environment variable RELPOS_ATTN_CFG=<0..5>

@@ -127,15 +127,17 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
   int best = t8 <= t4 ? 0 : 1;
   // Split: the full rounds of 8-wave units, then a last round whose heads
   // and tails (k per idle CU) take max(s + F, k*(T - s + F)) tiles with F =
-  // kSplitSegmentTiles per segment, plus the merge; considered when at most 4
-  // tails share a CU.
+  // kSplitSegmentTiles per segment, plus the merge, all at kSplitGridFactor
+  // times the unsplit per-tile cost; considered when at most 4 tails share a
+  // CU.
   if (allow_split) {
     constexpr int F = relpos::kSplitSegmentTiles;
     const relpos::SplitPlan sp = relpos::split_plan(g8, static_cast<int>(T), cus, F);
     if (sp.rest > 0 && sp.s < T && sp.k <= 4) {
       const int64_t head = sp.s + F, tails = static_cast<int64_t>(sp.k) * (T - sp.s + F);
       const int64_t last = head > tails ? head : tails;
-      const double ts = a8 * (sp.rounds + static_cast<double>(last + relpos::kMergeTiles) / static_cast<double>(T));
+      const double ts = a8 * relpos::kSplitGridFactor *
+                        (sp.rounds + static_cast<double>(last + relpos::kMergeTiles) / static_cast<double>(T));
       if (ts < (best == 0 ? t8 : t4)) best = relpos::kAttnSplitConfig;
     }
   }

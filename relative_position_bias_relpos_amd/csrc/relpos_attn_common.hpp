@@ -13,10 +13,15 @@ constexpr int kTileCols = 16;
 constexpr int kKStride = kD + 8;  // halves per K/V row in LDS (144 B)
 constexpr int kTileHalves = kTileKeys * kKStride;
 constexpr int kSlots = 4;               // LDS ring depth (power of two)
-#ifndef RELPOS_CHUNKS_PER_FENCE
-#define RELPOS_CHUNKS_PER_FENCE 8
-#endif
-constexpr int kChunksPerFence = RELPOS_CHUNKS_PER_FENCE;  // MFMA/VALU chunks between scheduling fences
+// MFMA/VALU chunks of a pipeline step between scheduling fences.  8-wave
+// workgroups (two waves per SIMD in one workgroup) run faster with the
+// interleave fixed chunk by chunk (64x64: 75.9 -> 74.3 us), 4- and 2-wave
+// workgroups with the compiler's own order inside the step (122.8 us against
+// 126.5 us at 48x80).
+template <int NW>
+constexpr int chunks_per_fence() {
+  return NW >= 8 ? 1 : 8;
+}
 constexpr float kGrowLimit = 32768.0f;  // 2^15: largest p allowed before m moves
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;

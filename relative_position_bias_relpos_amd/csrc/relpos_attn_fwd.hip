@@ -539,7 +539,7 @@ __device__ __forceinline__ void attn_segment(
       // registers 8*gg + 2*j of S half st map to P operand (2*st + gg), word j
       pcur[2 * st + (g >> 1)][2 * (g & 1)] = w0;
       pcur[2 * st + (g >> 1)][2 * (g & 1) + 1] = w1;
-      if ((i + 1) % kChunksPerFence == 0) __builtin_amdgcn_sched_barrier(0);
+      if ((i + 1) % chunks_per_fence<NW>() == 0) __builtin_amdgcn_sched_barrier(0);
     }
     load_rh(pn.kh);  // rel_h of tile t+1 (this tile's values are used); row 0 past the grid
 

@@ -67,6 +67,12 @@ constexpr int kSplitSegmentTiles = 6;
 // 96x96 favours the split.
 constexpr int kMergeTiles = 4;
 constexpr int kFusedPrologueTiles = 12;
+// Per-tile cost of the persistent split grid against an unsplit 8-wave
+// launch, beyond its segments and merge (per-segment staging of rel_h rows,
+// the piece stores; measured: 64x64 split 78.3-78.9 us against 75.4-75.6 us
+// unsplit where the tile model alone predicts 0.953 of it; 96x96 0.954 of
+// unsplit against a predicted 0.914).
+constexpr double kSplitGridFactor = 1.06;
 
 // Last-round split of configuration kAttnSplitConfig.  With `units` query
 // units of T key tiles on P workgroups (one per CU), `rounds` = units / P full

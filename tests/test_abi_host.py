@@ -200,13 +200,13 @@ def test_attn_config_with_workspace(lib):
     # 64x64, 12 heads: 192 units of 64 tiles on 256 CUs, no full round; the
     # 64 idle CUs take 3 tails each.  With 6 tiles per segment, s = (3*64 +
     # 2*6) / 4 = 51: head 51 + 6 = 57, tails 3 * (13 + 6) = 57, so
-    # 0.95 * (57 + 4) / 64 = 0.91 rounds against 0.95 unsplit -> split.
-    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == SPLIT
-    # 48x80, 2x12 heads: 360 units of 60 tiles: one full round, then 104
-    # units cut at s = 30 (k = 1): 0.95 * (1 + (36 + 4) / 60) = 1.58 against 1.77.
+    # 0.95 * 1.06 * (57 + 4) / 64 = 0.960 rounds against 0.95 unsplit -> no split.
+    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == 0
+    # 48x80, 2x12 heads: 360 units of 60 tiles: one full round, then 104 units
+    # cut at s = 30 (k = 1): 0.95 * 1.06 * (1 + (36 + 4) / 60) = 1.68 against 1.77.
     assert _cfg(lib, 2, 12, 48, 80, BF16, ws=1) == SPLIT
     # 96x96, 2x16 heads: 1152 units of 144 tiles: 4 rounds, then 128 cut at
-    # s = 72: 0.95 * (4 + (78 + 4) / 144) = 4.34 < 4.75.
+    # s = 72: 0.95 * 1.06 * (4 + (78 + 4) / 144) = 4.60 < 4.75.
     assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == SPLIT
     # fp16 64x64, 4x12 heads: 768 units = 3 whole rounds; splitting gains nothing.
     assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 1
@@ -218,13 +218,15 @@ def test_attn_config_with_workspace(lib):
 
 def test_workspace_bytes(lib):
     # two piece slots of (256*64 + 2*256) floats per compute unit
-    assert _ws_bytes(lib, 1, 12, 64, 64, BF16) == 256 * 2 * (256 * 64 + 512) * 4
+    assert _ws_bytes(lib, 2, 16, 96, 96, BF16) == 256 * 2 * (256 * 64 + 512) * 4
+    # 64x64, 12 heads on 256 CUs: the unsplit launch is chosen -> no workspace
+    assert _ws_bytes(lib, 1, 12, 64, 64, BF16) == 0
     # 64x64, 12 heads on 128 CUs: one full round of 128 units, then 64 units
-    # split at tile 32: 0.95 * (1 + (38 + 4) / 64) = 1.57 against 1.77.
+    # split at tile 32: 0.95 * 1.06 * (1 + (38 + 4) / 64) = 1.67 against 1.77.
     assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128, ws=1) == 5
     assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=128) == 128 * 2 * (256 * 64 + 512) * 4
     # 16x32 grid, 150 heads, 128 CUs: 300 units of 8 tiles, 2 rounds + 44
-    # split at tile 4: 0.95 * (2 + (10 + 4) / 8) = 3.56, no better than 2.77.
+    # split at tile 4: 0.95 * 1.06 * (2 + (10 + 4) / 8) = 3.78, no better than 2.77.
     assert _cfg(lib, 1, 150, 16, 32, BF16, cus=128, ws=1) == 1
     assert _ws_bytes(lib, 1, 150, 16, 32, BF16, cus=128) == 0
     # no split chosen -> 0; bad input -> -1

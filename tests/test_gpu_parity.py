@@ -219,7 +219,8 @@ def test_forced_split_full(name, kw, monkeypatch):
 @pytest.mark.parametrize("name,rows", [("deepencoder", 96), ("rect", 48), ("vitl", 32)])
 def test_split_full_size_sampled(name, rows, monkeypatch):
     """The split launch on the full-size workloads: chosen by the cost model
-    for 96x96, forced for 64x64 and 48x80 (where an unsplit launch is chosen)."""
+    for 96x96 (checked here) and 48x80, forced for 64x64 (where the unsplit
+    launch is chosen)."""
     from relative_position_bias_relpos_amd import binding as rp
     d = G.make(name)
     B, nh = d["q"].shape[:2]
