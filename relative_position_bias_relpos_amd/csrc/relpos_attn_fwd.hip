@@ -68,6 +68,11 @@ using namespace attn;
 // 64 banks once; with K's 72 halves the second group's rows fall on the first
 // group's banks.  Smaller workgroups keep 72 halves so that two of them still
 // fit a CU's LDS.
+// The plain launches copy a unit's rel_h rows to LDS with at most this many
+// 16-byte chunks per lane: 32 rows x H/4 chunks over 64 lanes, so H <= 72.
+constexpr int kRhLdsMaxChunks = 9;
+constexpr int kRhLdsMaxH = kRhLdsMaxChunks * 64 * 4 / 32;
+
 template <int NW>
 constexpr int v_stride() {
   return NW >= 8 ? 96 : kKStride;
@@ -413,23 +418,30 @@ __device__ __forceinline__ void attn_segment(
   const TilePos p2 = next_tile(p1, H);
   if constexpr (!FUSED && RH_LDS) {
     static_assert(ALIGNED, "rel_h rows are copied in 16-byte chunks");
-    // This wave's 32 rel_h rows: H/4 chunks of 16 bytes per row, 64/(H/4)
-    // rows per pass; rows past the grid read zeros (their outputs are not
+    // This wave's 32 rel_h rows, contiguous in memory: 16-byte chunk c = lane
+    // + 64*j is row c / (H/4), chunk c % (H/4) of it; at most kRhLdsMaxChunks
+    // per lane (H <= 72 on this path).  All loads are issued before the first
+    // LDS store.  Rows past the grid get zeros (their outputs are not
     // written).  The wave reads back only its own rows.
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int row0 = q0 + wu * 32;
-    const int nrows = N - row0 < 32 ? (N - row0 > 0 ? N - row0 : 0) : 32;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(rel_h + (head + (row0 < N ? row0 : 0)) * H, static_cast<uint32_t>(nrows * H) * 4);
     const int cpr = H / 4;
-    const int rpi = 64 / cpr;
-    const int lrow = lane / cpr, lcol = lane - lrow * cpr;
-    for (int r0 = 0; r0 < 32; r0 += rpi) {
-      const int row = r0 + lrow;
-      if (lrow < rpi && row < 32) {
-        const u32x4 x = buf_load16(rs, (row * H + 4 * lcol) * 4);
-        *reinterpret_cast<u32x4*>(rh_lds + (wu * 32 + row) * hs_l + 4 * lcol) = x;
-      }
+    const int nch = (N - row0 < 32 ? N - row0 : 32) * cpr;  // chunks inside the grid (<= 0: none)
+    const float* src = rel_h + (head + row0) * H;
+    const float rcp = 1.0f / static_cast<float>(cpr);
+    u32x4 x[kRhLdsMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kRhLdsMaxChunks; ++j) {
+      const int c = lane + 64 * j;
+      x[j] = c < nch ? *reinterpret_cast<const u32x4*>(src + 4 * c) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < kRhLdsMaxChunks; ++j) {
+      const int c = lane + 64 * j;
+      // c / cpr from the float product: (c + 0.5) / cpr is at least 1/(2 cpr)
+      // from the nearest integer, far more than the product's rounding error.
+      const int row = static_cast<int>((static_cast<float>(c) + 0.5f) * rcp);
+      if (c < 32 * cpr) *reinterpret_cast<u32x4*>(rh_lds + (wu * 32 + row) * hs_l + 4 * (c - row * cpr)) = x[j];
     }
   }
   if constexpr (FUSED) {
@@ -801,7 +813,8 @@ hipError_t launch_nw(const AttnArgs& a, hipStream_t stream) {
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
   if constexpr (NW == 8 && !FUSED) {
     // rel_h rows in LDS when they fit beside the ring (one workgroup per CU).
-    if (aligned && attn32_lds_bytes<8>() + fused_rh_lds_bytes(a.H) <= static_cast<size_t>(a.lds_limit)) {
+    if (aligned && a.H <= kRhLdsMaxH &&
+        attn32_lds_bytes<8>() + fused_rh_lds_bytes(a.H) <= static_cast<size_t>(a.lds_limit)) {
       return launch_cfg<BF16, OUT_F32, NW, true, SPLIT, false, true>(a, stream);
     }
   }
