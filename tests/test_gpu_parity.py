@@ -270,6 +270,21 @@ def test_split_workspace_reused_across_shapes(monkeypatch):
         assert torch.equal(out, _run_split(d, ws))
 
 
+@pytest.mark.parametrize("cfg", [0, 5])
+@pytest.mark.parametrize("H,W", [(12, 32), (72, 16), (76, 16)])
+def test_rel_h_rows_in_lds_shapes(cfg, H, W, monkeypatch):
+    """8-wave launches copy each unit's rel_h rows to LDS on tile-aligned grids
+    with H <= 72: a last unit whose upper waves lie past the grid (12x32: 384
+    queries), the largest H of that path (72: nine 16-byte chunks per lane, and
+    a half-empty last unit) and the first H past it (76: rel_h read from memory)."""
+    monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
+    d = G.make("tiny", H=H, W=W)
+    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda") if cfg == 5 else None
+    out = _run_split(d, ws)
+    ref, _, _ = G.oracle_full(d)
+    _check(f"cfg{cfg} rel_h rows {H}x{W}", np.abs(G.f64(out) - ref))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_forced_split_half_precision_output(dtype, monkeypatch):
     """The merge kernel's bf16/fp16 stores, against the oracle."""
