@@ -427,17 +427,22 @@ __device__ __forceinline__ void attn_segment(
     const int row0 = q0 + wu * 32;
     const int cpr = H / 4;
     const int nch = (N - row0 < 32 ? N - row0 : 32) * cpr;  // chunks inside the grid (<= 0: none)
+    // An opaque copy of the lane index keeps the per-chunk offsets from being
+    // hoisted out of the persistent kernel's loop over segments, where they
+    // would hold registers through the key loop.
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
     const float* src = rel_h + (head + row0) * H;
     const float rcp = 1.0f / static_cast<float>(cpr);
     u32x4 x[kRhLdsMaxChunks];
 #pragma unroll
     for (int j = 0; j < kRhLdsMaxChunks; ++j) {
-      const int c = lane + 64 * j;
+      const int c = ln + 64 * j;
       x[j] = c < nch ? *reinterpret_cast<const u32x4*>(src + 4 * c) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < kRhLdsMaxChunks; ++j) {
-      const int c = lane + 64 * j;
+      const int c = ln + 64 * j;
       // c / cpr from the float product: (c + 0.5) / cpr is at least 1/(2 cpr)
       // from the nearest integer, far more than the product's rounding error.
       const int row = static_cast<int>((static_cast<float>(c) + 0.5f) * rcp);
@@ -616,6 +621,18 @@ __device__ __forceinline__ void attn_segment(
   const int slot_last = (T - 1) & (kSlots - 1);
   step(0, True{}, sA, sB, pB, pA);
   int t = 1;
+  if constexpr (!SPLIT) {
+    // Unrolled by four: with t = 1 (mod 4) at each iteration every LDS slot
+    // of the four steps is a compile-time offset (no per-step address
+    // arithmetic; 64x64: 74.3 -> 71.2 us).  The persistent split kernel keeps
+    // the two-step loop: unrolled by four it spills registers.
+    for (; t + 3 < T; t += 4) {
+      step(t, False{}, sB, sA, pA, pB);
+      step(t + 1, False{}, sA, sB, pB, pA);
+      step(t + 2, False{}, sB, sA, pA, pB);
+      step(t + 3, False{}, sA, sB, pB, pA);
+    }
+  }
   for (; t + 1 < T; t += 2) {
     step(t, False{}, sB, sA, pA, pB);
     step(t + 1, False{}, sA, sB, pB, pA);
