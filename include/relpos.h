@@ -237,8 +237,8 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  * The choice compares times in workgroup rounds (one round = one 4-wave
  * workgroup per SIMD pair of every compute unit running all T key tiles of
  * its queries): configuration 0 counts every started round of its
- * workgroups as a full one, at 0.95 of a configuration-1 round for bf16
- * inputs (whose V conversion it shares) and 1.03 for fp16 (which needs none;
+ * workgroups as a full one, at 0.91 of a configuration-1 round for bf16
+ * inputs (whose V conversion it shares) and 0.985 for fp16 (which needs none;
  * both measured); configuration 1 counts a last round with at most one
  * workgroup per compute unit at 0.77 (a lone workgroup runs one wave per
  * SIMD, measured faster per tile); configuration 5 costs the 8-wave factor

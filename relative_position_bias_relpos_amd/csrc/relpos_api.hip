@@ -115,7 +115,7 @@ int device_props(DeviceProps* out) {
 int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool allow_split) {
   const int64_t N = H * W;
   const int64_t T = ((H + 3) / 4) * ((W + 15) / 16);  // key tiles per query unit
-  const double a8 = bf16 ? 0.95 : 1.03;
+  const double a8 = bf16 ? 0.91 : 0.985;
   // Configuration 0 (one workgroup per CU): every started round is a full
   // round.  Configuration 1 (two per CU): a last round with at most one
   // workgroup per CU runs those workgroups alone on their CUs.

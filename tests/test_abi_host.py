@@ -165,27 +165,30 @@ def test_attn_config_on_the_workloads(lib):
     # 48x80, 2x12 heads: 360 workgroups of 8 waves need two full rounds; 720
     # of 4 waves end with 208 lone workgroups -> 4 waves.
     assert _cfg(lib, 2, 12, 48, 80, BF16) == 1
-    # 96x96, 2x16 heads: 5 rounds x 0.95 = 4.75 against 4 + 0.77.
+    # 96x96, 2x16 heads: 5 rounds x 0.91 = 4.55 against 4 + 0.77.
     assert _cfg(lib, 2, 16, 96, 96, BF16) == 0
     # fp16 64x64, 4x12 heads: 3 rounds each; without a V conversion to share,
-    # an 8-wave round counts 1.03 -> 4 waves.
-    assert _cfg(lib, 4, 12, 64, 64, FP16) == 1
+    # an 8-wave round counts 0.985 -> 8 waves, by a small margin.
+    assert _cfg(lib, 4, 12, 64, 64, FP16) == 0
     assert _cfg(lib, 4, 12, 64, 64, BF16) == 0
 
 
 def test_attn_config_rounds_arithmetic(lib):
-    # One (b, h) of 64 queries: one 8-wave round (0.95) against one lone
+    # One (b, h) of 64 queries: one 8-wave round (0.91) against one lone
     # 4-wave workgroup (0.77).
     assert _cfg(lib, 1, 1, 8, 8, BF16) == 1
     # 512 heads of 256 queries: exactly two full 4-wave rounds (1024
-    # workgroups) against two 8-wave rounds at 0.95 (bf16) or 1.03 (fp16).
+    # workgroups) against two 8-wave rounds at 0.91 (bf16) or 0.985 (fp16).
     assert _cfg(lib, 1, 512, 16, 16, BF16) == 0
-    assert _cfg(lib, 1, 512, 16, 16, FP16) == 1
+    assert _cfg(lib, 1, 512, 16, 16, FP16) == 0
+    # fp16 still takes 4 waves where a lone last round decides: one (b, h) of
+    # 64 queries, 0.985 against 0.77.
+    assert _cfg(lib, 1, 1, 8, 8, FP16) == 1
     # 1024 heads of 128 queries: an 8-wave workgroup would be half empty
     # (four rounds) against two full 4-wave rounds.
     assert _cfg(lib, 1, 1024, 16, 8, BF16) == 1
     # The CU count enters: on 128 CUs the 64x64 workload needs two 8-wave
-    # rounds (1.9) against 384 = 1.5 rounds of 4 waves (1 + 0.77).
+    # rounds (1.82) against 384 = 1.5 rounds of 4 waves (1 + 0.77).
     assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128) == 1
 
 
@@ -200,16 +203,16 @@ def test_attn_config_with_workspace(lib):
     # 64x64, 12 heads: 192 units of 64 tiles on 256 CUs, no full round; the
     # 64 idle CUs take 3 tails each.  With 6 tiles per segment, s = (3*64 +
     # 2*6) / 4 = 51: head 51 + 6 = 57, tails 3 * (13 + 6) = 57, so
-    # 0.95 * 1.06 * (57 + 4) / 64 = 0.960 rounds against 0.95 unsplit -> no split.
+    # 0.91 * 1.06 * (57 + 4) / 64 = 0.919 rounds against 0.91 unsplit -> no split.
     assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == 0
     # 48x80, 2x12 heads: 360 units of 60 tiles: one full round, then 104 units
-    # cut at s = 30 (k = 1): 0.95 * 1.06 * (1 + (36 + 4) / 60) = 1.68 against 1.77.
+    # cut at s = 30 (k = 1): 0.91 * 1.06 * (1 + (36 + 4) / 60) = 1.61 against 1.77.
     assert _cfg(lib, 2, 12, 48, 80, BF16, ws=1) == SPLIT
     # 96x96, 2x16 heads: 1152 units of 144 tiles: 4 rounds, then 128 cut at
-    # s = 72: 0.95 * 1.06 * (4 + (78 + 4) / 144) = 4.60 < 4.75.
+    # s = 72: 0.91 * 1.06 * (4 + (78 + 4) / 144) = 4.41 < 4.55.
     assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == SPLIT
     # fp16 64x64, 4x12 heads: 768 units = 3 whole rounds; splitting gains nothing.
-    assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 1
+    assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 0
     # 16x16, 2 heads: 8 tiles in all, under 8 per CU -> no split.
     assert _cfg(lib, 1, 2, 16, 16, BF16, ws=1) in (0, 1)
     # without a workspace the split is never chosen
@@ -222,12 +225,13 @@ def test_workspace_bytes(lib):
     # 64x64, 12 heads on 256 CUs: the unsplit launch is chosen -> no workspace
     assert _ws_bytes(lib, 1, 12, 64, 64, BF16) == 0
     # 64x64, 12 heads on 128 CUs: one full round of 128 units, then 64 units
-    # split at tile 32: 0.95 * 1.06 * (1 + (38 + 4) / 64) = 1.67 against 1.77.
+    # split at tile 32: 0.91 * 1.06 * (1 + (38 + 4) / 64) = 1.60 against 1.77.
     assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128, ws=1) == 5
     assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=128) == 128 * 2 * (256 * 64 + 512) * 4
     # 16x32 grid, 150 heads, 128 CUs: 300 units of 8 tiles, 2 rounds + 44
-    # split at tile 4: 0.95 * 1.06 * (2 + (10 + 4) / 8) = 3.78, no better than 2.77.
-    assert _cfg(lib, 1, 150, 16, 32, BF16, cus=128, ws=1) == 1
+    # split at tile 4: 0.91 * 1.06 * (2 + (10 + 4) / 8) = 3.62; three 8-wave
+    # rounds (2.73) beat 2 + 0.77 4-wave rounds.
+    assert _cfg(lib, 1, 150, 16, 32, BF16, cus=128, ws=1) == 0
     assert _ws_bytes(lib, 1, 150, 16, 32, BF16, cus=128) == 0
     # no split chosen -> 0; bad input -> -1
     assert _ws_bytes(lib, 4, 12, 64, 64, FP16) == 0
