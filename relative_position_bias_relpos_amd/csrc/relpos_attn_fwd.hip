@@ -181,9 +181,13 @@ __device__ __forceinline__ void fused_bias_rows(const u32x4 (&qf)[4], const uint
   for (int p = W + half; p < Ws; p += 2) sw[j * Ws + p] = -__builtin_inff();
 }
 
-// A piece: a workgroup's partial result for one unit -- O (unnormalised,
-// BM x 64), then the reference maximum m and the row sum l of each query.
-// Unit i of the split last round keeps its head in slot 2i, its tail in 2i+1.
+// A piece: a workgroup's partial result for one unit -- O / l in fp16 (BM x
+// 64 halves, in the first half of the BM x 64 floats the slot reserves), then
+// the reference maximum m and the row sum l of each query (fp32).  O / l is a
+// weighted mean of V rows, so it is within V's fp16 range; the merge takes a
+// convex combination of the two pieces' O / l, so their fp16 rounding (2^-11
+// relative) bounds its error.  Unit i of the split last round keeps its head in
+// slot 2i, its tail in 2i+1.
 template <int BM>
 constexpr int64_t piece_floats() {
   return static_cast<int64_t>(BM) * kD + 2 * BM;
@@ -651,16 +655,18 @@ __device__ __forceinline__ void attn_segment(
   if constexpr (SPLIT) {
     const int unit_tiles = band_tiles * ((W + kTileCols - 1) / kTileCols);
     if (nt != unit_tiles) {
-      // One piece of a split unit: O (unnormalised), m and l go to the
+      // One piece of a split unit: O / l (fp16), m and l go to the
       // workspace; split_merge_kernel combines the pieces after this launch.
       float* pw = ws + static_cast<int64_t>(slot) * piece_floats<BM>();
+      uint16_t* po = reinterpret_cast<uint16_t*>(pw);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * dt + 8 * g + 4 * half;
-          *reinterpret_cast<f32x4*>(pw + ql * kD + d) =
-              f32x4{acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+          *reinterpret_cast<u32x2*>(po + ql * kD + d) =
+              u32x2{pack_f16(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
+                    pack_f16(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
         }
       if (half == 0) {
         pw[BM * kD + ql] = m;
@@ -710,14 +716,21 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
   const float* pt = ph + piece_floats<BM>();
   const float mh = ph[BM * kD + ql], mt = pt[BM * kD + ql];
   const float lh = ph[BM * kD + BM + ql], lt = pt[BM * kD + BM + ql];
-  const f32x4 xh = *reinterpret_cast<const f32x4*>(ph + ql * kD + c);
-  const f32x4 xt = *reinterpret_cast<const f32x4*>(pt + ql * kD + c);
+  const u32x2 xh = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(ph) + ql * kD + c);
+  const u32x2 xt = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(pt) + ql * kD + c);
   const float mx = __builtin_fmaxf(mh, mt);
-  const float wh = exp2_fast(mh - mx), wt = exp2_fast(mt - mx);
-  const float inv = 1.0f / (lh * wh + lt * wt);
+  // The pieces' weights: l * exp2(m - max), normalised to sum to one.
+  const float wh0 = lh * exp2_fast(mh - mx), wt0 = lt * exp2_fast(mt - mx);
+  const float inv = 1.0f / (wh0 + wt0);
+  const float wh = wh0 * inv, wt = wt0 * inv;
   f32x4 o4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o4[e] = (xh[e] * wh + xt[e] * wt) * inv;
+  for (int e = 0; e < 2; ++e) {
+    const f32x2 a = unpack_f16(xh[e]);
+    const f32x2 b = unpack_f16(xt[e]);
+    o4[2 * e] = a[0] * wh + b[0] * wt;
+    o4[2 * e + 1] = a[1] * wh + b[1] * wt;
+  }
   const size_t row = static_cast<size_t>(bh) * N + qi;
   if constexpr (OUT_F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * kD + c) = o4;

@@ -42,6 +42,11 @@ __device__ __forceinline__ uint32_t as_uint(float x) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Packed fp16 pair -> two fp32 (exact).
+__device__ __forceinline__ f32x2 unpack_f16(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+
 // Two fp32 -> packed fp16 pair (round to nearest even; overflow gives inf).
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   f32x2 v = {lo, hi};
