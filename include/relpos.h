@@ -146,8 +146,8 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
  * ceil(rest / (P - rest)), rounded to nearest): their heads [0, s) run on
  * `rest` workgroups and their tails [s, T) on the others, k per workgroup;
  * s balances s + 6 against k*(T - s + 6), 6 tiles being the measured fixed
- * cost of one segment.  Heads and tails store their unnormalised
- * output, reference maximum and row sum in the workspace, and a second
+ * cost of one segment.  Heads and tails store their normalised output
+ * (fp16), reference maximum and row sum in the workspace, and a second
  * kernel on the same stream merges each unit's head and tail (in that order)
  * and writes its output.  Results are bitwise reproducible run to run, and
  * differ from the unsplit launch by rounding only.
