@@ -37,7 +37,8 @@
 //     matrix cores run while the VALU does exp/convert work.  Then it stores
 //     the registers holding tile t+2 into slot (t+2)%4 and starts the global
 //     loads of tile t+3.  The loop is unrolled by two with the S and P register
-//     sets swapping roles, so no copies are made between steps.
+//     sets swapping roles, so no copies are made between steps, and by four
+//     where registers allow (every LDS slot offset then a constant).
 //
 // Online softmax (exp2 domain, scores pre-multiplied by log2 e)
 //   * Each query row keeps a reference maximum m.  Per tile,
