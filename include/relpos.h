@@ -231,10 +231,13 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  *   0: workgroups of 8 waves x 32 queries, one workgroup per compute unit;
  *      a workgroup's two waves per SIMD share one K/V staging.
  *   1: workgroups of 4 waves x 32 queries, two per compute unit.
+ *   3: workgroups of 4 waves x 16 queries (16x16x32 MFMA), chosen when a
+ *      unit has at most 4 key tiles of 4 x 16 grid cells (ceil(H/4) *
+ *      ceil(W/16) <= 4), where its shorter pipeline is measured fastest.
  *   5: configuration 0 with the key range split over one workgroup per
  *      compute unit (relpos_attn_fwd_ws only).
  *
- * The choice compares times in workgroup rounds (one round = one 4-wave
+ * Otherwise the choice compares times in workgroup rounds (one round = one 4-wave
  * workgroup per SIMD pair of every compute unit running all T key tiles of
  * its queries): configuration 0 counts every started round of its
  * workgroups as a full one, at 0.91 of a configuration-1 round for bf16

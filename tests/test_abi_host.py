@@ -174,22 +174,33 @@ def test_attn_config_on_the_workloads(lib):
 
 
 def test_attn_config_rounds_arithmetic(lib):
-    # One (b, h) of 64 queries: one 8-wave round (0.91) against one lone
-    # 4-wave workgroup (0.77).
-    assert _cfg(lib, 1, 1, 8, 8, BF16) == 1
-    # 512 heads of 256 queries: exactly two full 4-wave rounds (1024
-    # workgroups) against two 8-wave rounds at 0.91 (bf16) or 0.985 (fp16).
-    assert _cfg(lib, 1, 512, 16, 16, BF16) == 0
-    assert _cfg(lib, 1, 512, 16, 16, FP16) == 0
+    # One (b, h) of 256 queries (32x8 grid, 8 key tiles): one 8-wave round
+    # (0.91) against two lone 4-wave workgroups (0.77).
+    assert _cfg(lib, 1, 1, 32, 8, BF16) == 1
+    # 512 heads of 256 queries (32x8 grids): exactly two full 4-wave rounds
+    # (1024 workgroups) against two 8-wave rounds at 0.91 (bf16) or 0.985 (fp16).
+    assert _cfg(lib, 1, 512, 32, 8, BF16) == 0
+    assert _cfg(lib, 1, 512, 32, 8, FP16) == 0
     # fp16 still takes 4 waves where a lone last round decides: one (b, h) of
-    # 64 queries, 0.985 against 0.77.
-    assert _cfg(lib, 1, 1, 8, 8, FP16) == 1
-    # 1024 heads of 128 queries: an 8-wave workgroup would be half empty
-    # (four rounds) against two full 4-wave rounds.
-    assert _cfg(lib, 1, 1024, 16, 8, BF16) == 1
+    # 256 queries, 0.985 against 0.77.
+    assert _cfg(lib, 1, 1, 32, 8, FP16) == 1
+    # 1024 heads of 128 queries (32x4 grids): an 8-wave workgroup would be
+    # half empty (four rounds) against two full 4-wave rounds.
+    assert _cfg(lib, 1, 1024, 32, 4, BF16) == 1
     # The CU count enters: on 128 CUs the 64x64 workload needs two 8-wave
     # rounds (1.82) against 384 = 1.5 rounds of 4 waves (1 + 0.77).
     assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128) == 1
+
+
+def test_attn_config_short_key_loops(lib):
+    # At most 4 key tiles of 4x16 cells per unit -> configuration 3, the
+    # 16-query kernel: 14x14 windows (4 tiles), the 16x16 grid (4), 8x32 (4).
+    assert _cfg(lib, 25, 12, 14, 14, BF16) == 3
+    assert _cfg(lib, 1, 2, 16, 16, BF16) == 3
+    assert _cfg(lib, 1, 2, 8, 32, FP16) == 3
+    assert _cfg(lib, 25, 12, 14, 14, BF16, ws=1) == 3
+    # 5 tiles (20x16) and more go to the rounds model.
+    assert _cfg(lib, 1, 2, 20, 16, BF16) in (0, 1)
 
 
 def test_attn_config_rejects_bad_input(lib):
@@ -213,8 +224,8 @@ def test_attn_config_with_workspace(lib):
     assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == SPLIT
     # fp16 64x64, 4x12 heads: 768 units = 3 whole rounds; splitting gains nothing.
     assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 0
-    # 16x16, 2 heads: 8 tiles in all, under 8 per CU -> no split.
-    assert _cfg(lib, 1, 2, 16, 16, BF16, ws=1) in (0, 1)
+    # 16x16, 2 heads: 4 key tiles per unit -> the 16-query kernel, split or not.
+    assert _cfg(lib, 1, 2, 16, 16, BF16, ws=1) == 3
     # without a workspace the split is never chosen
     assert _cfg(lib, 1, 12, 64, 64, BF16, ws=0) == 0
 

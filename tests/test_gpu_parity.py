@@ -167,12 +167,12 @@ def test_each_launch_config(cfg, name, kw, monkeypatch):
     _check(f"cfg{cfg} {name}", np.abs(G.f64(out) - ref))
 
 
-@pytest.mark.parametrize("name", ["deepencoder", "rect", "batched_fp16"])
+@pytest.mark.parametrize("name", ["deepencoder", "rect", "batched_fp16", "windowed"])
 def test_automatic_config_matches_its_prediction(name, monkeypatch):
     """Without RELPOS_ATTN_CFG the library launches the configuration that
     relpos_attn_config predicts for this device: same bits as forcing it."""
     from relative_position_bias_relpos_amd import binding as rp
-    d = G.make(name)  # full size: configuration 0 for the 64x64 grids, 1 for 48x80
+    d = G.make(name)  # full size: configuration 0 for the 64x64 grids, 1 for 48x80, 3 for the windows
     monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
     auto, _, _ = G.gpu_run(d)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
