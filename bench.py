@@ -6,7 +6,7 @@ relpos_attn_fwd, on the DeepEncoder global-attention workload (B=1, 12 heads,
 relpos_attn_fused (the same step in one launch, bias computed in the attention
 kernel) is timed beside it.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 200] [--workload deepencoder]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--settle-ms 300] [--workload deepencoder]
 """
 
 import argparse
@@ -134,6 +134,53 @@ def dense_sdpa_context(w, q, k, v, rel_h, rel_w, ours, out, rounds=3):
         return {"kind": "context: dense bias + torch SDPA", "unavailable": f"{type(e).__name__}: {e}"[:200]}
 
 
+def gpu_clocks(dev_index=0):
+    """Current graphics and memory clocks (MHz) of the GPU torch uses, from
+    amdsmi; None where the query is not available."""
+    try:
+        import amdsmi
+        import torch
+
+        amdsmi.amdsmi_init()
+        try:
+            handles = amdsmi.amdsmi_get_processor_handles()
+            handle = handles[0] if handles else None
+            props = torch.cuda.get_device_properties(dev_index)
+            want = getattr(props, "pci_bus_id", None)
+            for h in handles:
+                try:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if want is not None and int(bdf.split(":")[1], 16) == int(want):
+                        handle = h
+                        break
+                except Exception:
+                    pass
+            if handle is None:
+                return None
+            g = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+            m = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.MEM)
+            return {"sclk_mhz": g.get("clk"), "sclk_max_mhz": g.get("max_clk"),
+                    "mclk_mhz": m.get("clk"), "mclk_max_mhz": m.get("max_clk")}
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # no amdsmi, or no permission: report, never fail the bench
+        return {"unavailable": f"{type(e).__name__}: {e}"[:120]}
+
+
+def rocm_version():
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def stats_ms(xs):
+    import statistics
+    return {"mean": round(sum(xs) / len(xs), 5), "median": round(statistics.median(xs), 5),
+            "min": round(min(xs), 5), "max": round(max(xs), 5)}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -149,8 +196,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU clock needs about 20 ms of work to settle")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed ones")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back steps for this long (wall clock) before the warm-up, so the "
+                         "GPU clock has ramped up; recorded in the output line")
     ap.add_argument("--workload", default="deepencoder")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -212,37 +261,75 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    clocks_idle = gpu_clocks()
+    # Clock settle: back-to-back steps (and fused calls) for --settle-ms of wall
+    # time, synchronised every 20 so the queue stays short.
+    settle_calls = 0
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+            fused()
+        settle_calls += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
         fused()
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
+    clocks_before = gpu_clocks()
 
-    # Whole steps (build + attention), HIP events on the launch stream.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: exactly K steps bracketed by synchronisations; HIP events
+    # on the launch stream (torch's current stream, which the binding passes)
+    # before the build, between the two calls and after the attention call.
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
+    for i in range(K):
+        ev[i][0].record()
+        build()
+        ev[i][1].record()
+        attn()
+        ev[i][2].record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    build_calls = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_calls = [e[1].elapsed_time(e[2]) for e in ev]
+    clocks_after = gpu_clocks()
 
-    # Per-kernel average launch durations over back-to-back launches.
-    def time_loop(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
-
-    attn_ms = time_loop(attn, args.steps)
-    build_ms = time_loop(build, args.steps)
-    fused_ms = time_loop(fused, args.steps)
+    # The fused call, timed the same way in its own loop.
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        fev[i][0].record()
+        fused()
+        fev[i][1].record()
+    torch.cuda.synchronize()
+    fused_calls = [e[0].elapsed_time(e[1]) for e in fev]
     mem_after = torch.cuda.memory_allocated()
+
+    # Host cost of one attention call (binding + argument checks + launch),
+    # enqueued back to back without synchronising; and of the C call alone
+    # with the arguments already marshalled.
+    n_host = 200
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_host):
+        attn()
+    host_us = (time.perf_counter() - t0) / n_host * 1e6
+    torch.cuda.synchronize()
+    lib = rp._load()
+    cargs = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(rel_h), rp._ptr(rel_w), rp._ptr(out),
+             w.B, w.heads, H, W, w.D, float(scale), rp._DT[q.dtype], rp._DT[out.dtype], rp._stream(q))
+    t0 = time.perf_counter()
+    for _ in range(n_host):
+        lib.relpos_attn_fwd(*cargs)
+    c_us = (time.perf_counter() - t0) / n_host * 1e6
+    torch.cuda.synchronize()
+
+    attn_ms = sum(attn_calls) / K
+    build_ms = sum(build_calls) / K
+    fused_ms = sum(fused_calls) / K
 
     # Output check on sampled rows of the last call (two heads) against the oracle
     # is left to the test-suite; here only finiteness is asserted.
@@ -279,10 +366,21 @@ def main():
             "global_batch": w.B, "parallelism": "none (1 GPU)",
         },
         "attn_ms_per_call": round(attn_ms, 5),
+        "attn_ms_per_call_stats": stats_ms(attn_calls),
         "attn_tflops": round(attn_tflops, 2),
+        "attn_tflops_at_median": round(flops / (stats_ms(attn_calls)["median"] * 1e-3) / 1e12, 2),
         "attn_pct_bf16_peak": round(100.0 * attn_tflops / PEAK_TFLOPS, 2),
         "build_ms_per_call": round(build_ms, 5),
+        "build_ms_per_call_stats": stats_ms(build_calls),
         "build_gbs": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
+        "timing": "HIP events on the launch stream around every call of the timed steps; "
+                  "ms_per_step = first event to last / steps; *_ms_per_call = mean of the per-call events",
+        "settle": {"ms": args.settle_ms, "calls": settle_calls,
+                   "what": "untimed back-to-back steps and fused calls before the warm-up (clock ramp)"},
+        "clocks": {"idle_before_settle": clocks_idle, "before_timed": clocks_before, "after_timed": clocks_after},
+        "rocm": rocm_version(),
+        "torch_hip": torch.version.hip,
+        "host_us_per_attn_call": {"python_binding": round(host_us, 2), "c_call_only": round(c_us, 2)},
         "roofline": {
             "bound": "mfma",
             "kernel": "relpos_attn_fwd",
@@ -296,6 +394,7 @@ def main():
         "fused": {
             "call": "relpos_attn_fused (bias rows computed in the attention kernel; no rel_h/rel_w tensors)",
             "ms_per_call": round(fused_ms, 5),
+            "ms_per_call_stats": stats_ms(fused_calls),
             "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
             "pct_bf16_peak": round(100.0 * flops / (fused_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
             "workspace_bytes": ws_fused.numel(),

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 3
+#define RELPOS_ABI_VERSION 4
 
 typedef enum relpos_dtype {
   RELPOS_BF16 = 0,
@@ -111,10 +111,18 @@ relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel
  *   H, W       >= 1, H*W <= 2^24, H <= 4096, W <= 4096, and
  *              B*heads*ceil(H*W/64) < 2^31
  *   D          must be 64
- *   scale      finite (else E_VALUE); multiplies q.k only (not the bias)
+ *   scale      multiplies q.k only (not the bias); any sign.  It must be 0
+ *              or satisfy 2^-64 <= |scale| < inf, else E_VALUE (the kernel
+ *              adds rel_w / scale to the q.k accumulator; scale == 0 is
+ *              computed exactly as the bias alone)
  *   in_dtype   RELPOS_BF16 or RELPOS_FP16
  *   out_dtype  RELPOS_FP32, or equal to in_dtype
  *   stream     hipStream_t to enqueue on
+ * Value range: P.V runs on fp16 MFMA (P in fp16, fp32 accumulation), so bf16
+ * v is converted to fp16 when staged: |v| must stay below 65520 (larger
+ * values become inf and the outputs they reach are not finite), and
+ * |v| < 2^-24 is flushed to zero (absolute error below 2^-25).  fp16 v is
+ * used as is.  Nothing checks the range.
  * Errors: E_SHAPE, E_DTYPE, E_VALUE, E_NULL, E_ALIGN, E_DEVICE, E_ALIAS, E_LAUNCH.
  */
 relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
@@ -191,7 +199,8 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  * split would not be faster (max(s + 12, k*(T - s + 12)) + 4 >= T + 12).
  *
  * Arguments: q, k, v, out, B, heads, H, W, D, scale, in_dtype, out_dtype and
- * stream as for relpos_attn_fwd, plus
+ * stream as for relpos_attn_fwd (with the same scale rule and bf16 v range),
+ * plus
  *   rel_pos_h  [2H-1, D]  in_dtype (device)
  *   rel_pos_w  [2W-1, D]  in_dtype (device)
  *   workspace  device scratch, 16-byte aligned, not overlapping any other
@@ -248,15 +257,31 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  * times 1.06 (the persistent grid's measured per-tile overhead) times (full
  * rounds + (max(s + 6, k*(T - s + 6)) + 4) / T) in the terms of
  * relpos_attn_fwd_ws, and is considered only with a workspace, a last round
- * to split and k <= 4.  Ties go to the lower
- * number.  Inside the calls the environment variable RELPOS_ATTN_CFG=<0..5>
- * overrides the choice (2..4 are slower alternatives kept for comparison;
- * 5 only where a large enough workspace is passed).
+ * to split and k <= 4.  Ties go to the lower number.
  * Returns -1 if a size or the dtype is out of range (as relpos_attn_fwd
  * checks them) or cu_count < 1.
  */
 int relpos_attn_config(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
                        int cu_count, int with_workspace);
+
+/*
+ * relpos_attn_fwd_cfg: relpos_attn_fwd_ws in a launch configuration chosen by
+ * the caller instead of relpos_attn_config's model, for measuring and testing
+ * the configurations against each other.
+ *
+ * Same operation, arguments, tolerance and errors as relpos_attn_fwd_ws, plus
+ *   config  one of the configurations listed with relpos_attn_config, or -1
+ *           for the automatic choice (then exactly relpos_attn_fwd_ws).  Any
+ *           other value is E_VALUE; a configuration whose LDS does not fit the
+ *           device is E_SHAPE.  Configuration 5 needs the workspace
+ *           relpos_attn_workspace_bytes reports for a split problem (E_NULL
+ *           without one, E_SHAPE if too small); the others ignore it.
+ */
+relpos_status relpos_attn_fwd_cfg(const void* q, const void* k, const void* v,
+                                  const float* rel_h, const float* rel_w, void* out,
+                                  int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                  float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                  int config, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* relpos_status_string(relpos_status s);

@@ -62,6 +62,9 @@ def _load():
         lib.relpos_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         lib.relpos_attn_config.restype = i32
         lib.relpos_attn_config.argtypes = [i64, i64, i64, i64, i32, i32, i32]
+        lib.relpos_attn_fwd_cfg.restype = i32
+        lib.relpos_attn_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32,
+                                            i32, vp, i64, vp]
         _lib = lib
         return lib
 
@@ -74,10 +77,10 @@ def abi_version():
     return _load().relpos_abi_version()
 
 
-def attn_config(B, heads, H, W, dtype, cu_count, with_workspace=True):
+def attn_config(B, heads, H, W, dtype, cu_count, with_workspace=False):
     """Launch configuration the attention call uses for this problem on a
     device with `cu_count` compute units (0: 8-wave workgroups, 1: 4-wave,
-    5: key range split, only with a workspace); host-only."""
+    3: 16-query waves, 5: key range split, only with a workspace); host-only."""
     c = _load().relpos_attn_config(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count),
                                    1 if with_workspace else 0)
     if c < 0:
@@ -102,7 +105,7 @@ def fused_workspace_bytes(B, heads, H, W, dtype, cu_count):
 
 
 _cus = {}
-_workspaces = {}  # (device index, stream handle) -> uint8 scratch tensor
+_workspaces = {}  # (device index, stream handle) -> uint8 scratch tensor of relpos_attn_fused
 
 
 def _cu_count(device):
@@ -112,8 +115,9 @@ def _cu_count(device):
 
 
 def _cached_workspace(device, stream, nbytes):
-    """A scratch workspace of at least `nbytes` for one (device, stream); calls
-    on one stream never overlap, so it is reused as is."""
+    """relpos_attn_fused's scratch workspace for one (device, stream): calls on
+    one stream never overlap, so it is reused, grown when a larger problem
+    needs more, and kept until release_workspaces()."""
     key = (device.index, stream)
     with _lock:
         ws = _workspaces.get(key)
@@ -121,6 +125,19 @@ def _cached_workspace(device, stream, nbytes):
             ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
             _workspaces[key] = ws
         return ws
+
+
+def cached_workspace_bytes():
+    """Bytes held by the workspaces relpos_attn_fused(workspace="auto") keeps."""
+    with _lock:
+        return sum(w.numel() for w in _workspaces.values())
+
+
+def release_workspaces():
+    """Drop the cached relpos_attn_fused workspaces (the memory returns to
+    torch's allocator once the work queued on their streams has finished)."""
+    with _lock:
+        _workspaces.clear()
 
 
 def _ptr(t):
@@ -178,13 +195,16 @@ def relpos_build(q, rel_pos_h, rel_pos_w, H, W, rel_h=None, rel_w=None):
 
 
 def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torch.float32,
-                    workspace="auto"):
+                    workspace=None, config=None):
     """out [B,heads,H*W,D] = softmax(scale*q.k + rel_h[:, j/W] + rel_w[:, j%W]) @ v.
 
-    workspace: "auto" (default) calls relpos_attn_fwd_ws with a scratch
-    workspace cached per (device, stream), allocated on the first call that
-    needs one; a tensor is used as the workspace; None calls relpos_attn_fwd
-    (no key-range split).
+    workspace: None (default) calls relpos_attn_fwd, which needs no scratch
+    memory; a uint8 device tensor calls relpos_attn_fwd_ws, which may then
+    split the key range of the last round of query units across idle compute
+    units (workspace_bytes() says how much it needs; 0 means no split).
+    config: None for the library's own choice of launch configuration, or one
+    of the configurations include/relpos.h lists (relpos_attn_fwd_cfg; for
+    measurements and tests).
     """
     lib = _load()
     B, nh, D = _dims(q, H, W)
@@ -203,22 +223,24 @@ def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torc
     _need(out, "out")
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
-    if workspace is None:
+    if workspace is not None and not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be None or a device tensor")
+    ws_ptr = _ptr(workspace)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if config is not None:
+        st = lib.relpos_attn_fwd_cfg(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                                     B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
+                                     int(config), ws_ptr, ws_len, _stream(q))
+        _check("relpos_attn_fwd_cfg", st)
+    elif workspace is None:
         st = lib.relpos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
                                  B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype], _stream(q))
         _check("relpos_attn_fwd", st)
-        return out
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError('workspace must be "auto", None or a tensor')
-        need = workspace_bytes(B, nh, H, W, q.dtype, _cu_count(q.device))
-        workspace = _cached_workspace(q.device, _stream(q).value, need) if need > 0 else None
-    ws_ptr = _ptr(workspace)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.relpos_attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
-                                B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
-                                ws_ptr, ws_len, _stream(q))
-    _check("relpos_attn_fwd_ws", st)
+    else:
+        st = lib.relpos_attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                                    B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
+                                    ws_ptr, ws_len, _stream(q))
+        _check("relpos_attn_fwd_ws", st)
     return out
 
 
@@ -228,7 +250,8 @@ def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_
     q, k, v and the tables, without rel_h/rel_w tensors.
 
     workspace: "auto" (default) uses a scratch workspace cached per (device,
-    stream); a tensor is used as the workspace.
+    stream) until release_workspaces(); a uint8 device tensor of at least
+    fused_workspace_bytes() is used as given.
     """
     lib = _load()
     B, nh, D = _dims(q, H, W)

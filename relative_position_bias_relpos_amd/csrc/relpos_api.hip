@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <cstdlib>
 #include <mutex>
 
 #include "relpos_kernels.hpp"
@@ -38,6 +37,14 @@ relpos_status check_dims(int64_t B, int64_t heads, int64_t H, int64_t W, int64_t
 
 bool is_half(relpos_dtype t) { return t == RELPOS_BF16 || t == RELPOS_FP16; }
 
+// The attention kernels fold rel_w / scale into the q.k accumulator, so a
+// nonzero scale must keep 1/scale finite with room to spare: 0, or
+// 2^-64 <= |scale| < inf.
+bool scale_ok(float scale) {
+  if (!std::isfinite(scale)) return false;
+  return scale == 0.0f || std::fabs(scale) >= 0x1p-64f;
+}
+
 relpos_status check_align(const Operand* ops, int n) {
   for (int i = 0; i < n; ++i) {
     if (ops[i].p == nullptr) return RELPOS_E_NULL;
@@ -49,15 +56,29 @@ relpos_status check_align(const Operand* ops, int n) {
 }
 
 // Every operand must be device memory of the current device, and its
-// allocation must hold the whole operand.  Failed queries leave no sticky
-// HIP error behind.
+// allocation must hold the whole operand.  Each allocation is queried once:
+// an operand inside a range an earlier operand of the same call already
+// resolved needs no query (q, k and v cut from one qkv tensor cost one).
+// Failed queries leave no sticky HIP error behind.
 relpos_status check_device(const Operand* ops, int n) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return RELPOS_E_HIP;
   }
+  uintptr_t lo[8], hi[8];
+  int known = 0;
   for (int i = 0; i < n; ++i) {
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(ops[i].p);
+    const uintptr_t p1 = p0 + ops[i].bytes;
+    bool inside = false;
+    for (int j = 0; j < known && !inside; ++j) inside = p0 >= lo[j] && p0 < hi[j];
+    if (inside) {
+      for (int j = 0; j < known; ++j) {
+        if (p0 >= lo[j] && p0 < hi[j] && p1 > hi[j]) return RELPOS_E_SHAPE;
+      }
+      continue;
+    }
     hipPointerAttribute_t attr;
     if (hipPointerGetAttributes(&attr, ops[i].p) != hipSuccess) {
       (void)hipGetLastError();
@@ -71,9 +92,13 @@ relpos_status check_device(const Operand* ops, int n) {
       (void)hipGetLastError();
       return RELPOS_E_DEVICE;
     }
-    const uintptr_t p0 = reinterpret_cast<uintptr_t>(ops[i].p);
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-    if (p0 + ops[i].bytes > b0 + size) return RELPOS_E_SHAPE;
+    if (p1 > b0 + size) return RELPOS_E_SHAPE;
+    if (known < 8) {
+      lo[known] = b0;
+      hi[known] = b0 + size;
+      ++known;
+    }
   }
   return RELPOS_OK;
 }
@@ -151,30 +176,24 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
 
 // Order in which attention configurations are tried when the chosen one does
 // not fit the device's LDS.
-constexpr int kAttnFallback[] = {0, 1, 2, 3, 4};
+constexpr int kAttnFallback[] = {0, 1, 3};
 
-// Tuning knob: RELPOS_ATTN_CFG=<0..5> forces one configuration when it fits
-// (read on every call, so one process can compare configurations); 5 only
-// applies where a workspace is passed.
-int forced_attn_config() {
-  const char* e = std::getenv("RELPOS_ATTN_CFG");
-  if (!e || !*e) return -1;
-  const int c = std::atoi(e);
-  return (c >= 0 && c < relpos::attn_num_configs()) ? c : -1;
-}
+bool config_known(int c) { return c == 0 || c == 1 || c == 3 || c == relpos::kAttnSplitConfig; }
 
-// Shared body of relpos_attn_fwd and relpos_attn_fwd_ws.
+// Shared body of relpos_attn_fwd, relpos_attn_fwd_ws and relpos_attn_fwd_cfg
+// (forced >= 0: that configuration, which must fit the device's LDS).
 relpos_status attn_fwd_impl(const void* q, const void* k, const void* v,
                             const float* rel_h, const float* rel_w, void* out,
                             int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
                             float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
-                            bool with_ws, void* workspace, int64_t workspace_bytes, void* stream) {
+                            bool with_ws, void* workspace, int64_t workspace_bytes, void* stream,
+                            int forced) {
   int64_t BH = 0;
   relpos_status st = check_dims(B, heads, H, W, D, &BH);
   if (st != RELPOS_OK) return st;
   if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
   if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
-  if (!std::isfinite(scale)) return RELPOS_E_VALUE;
+  if (!scale_ok(scale)) return RELPOS_E_VALUE;
   if (BH == 0) return RELPOS_OK;
   // Workgroup counts (down to 64 queries each) must fit a 1-D grid.
   if (BH * ((H * W + 63) / 64) >= (int64_t(1) << 31)) return RELPOS_E_SHAPE;
@@ -200,10 +219,9 @@ relpos_status attn_fwd_impl(const void* q, const void* k, const void* v,
   const bool bf16 = in_dtype == RELPOS_BF16;
   // The workspace is used (and checked) only when the split is chosen.
   const size_t need = relpos::attn_split_workspace_bytes(BH, H * W, props.cus);
-  const bool can_split = with_ws && workspace != nullptr && static_cast<uint64_t>(workspace_bytes) >= need;
-  int cfg = forced_attn_config();
-  if (cfg == relpos::kAttnSplitConfig && !can_split) cfg = -1;
-  if (cfg < 0 || !fits(cfg)) cfg = attn_auto_config(BH, H, W, bf16, props.cus, with_ws);
+  int cfg = forced;
+  if (cfg >= 0 && !fits(cfg)) return RELPOS_E_SHAPE;
+  if (cfg < 0) cfg = attn_auto_config(BH, H, W, bf16, props.cus, with_ws);
   if (cfg == relpos::kAttnSplitConfig) {
     if (workspace == nullptr) return RELPOS_E_NULL;
     ops[6] = Operand{workspace, need};
@@ -305,7 +323,7 @@ relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
                               float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
                               void* stream) {
   return attn_fwd_impl(q, k, v, rel_h, rel_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
-                       false, nullptr, 0, stream);
+                       false, nullptr, 0, stream, -1);
 }
 
 int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t W, relpos_dtype in_dtype,
@@ -334,7 +352,7 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
   if (st != RELPOS_OK) return st;
   if (!is_half(in_dtype)) return RELPOS_E_DTYPE;
   if (out_dtype != RELPOS_FP32 && out_dtype != in_dtype) return RELPOS_E_DTYPE;
-  if (!std::isfinite(scale) || workspace_bytes < 0) return RELPOS_E_VALUE;
+  if (!scale_ok(scale) || workspace_bytes < 0) return RELPOS_E_VALUE;
   if (BH == 0) return RELPOS_OK;
   if (BH * ((H * W + 63) / 64) >= (int64_t(1) << 31)) return RELPOS_E_SHAPE;
 
@@ -388,7 +406,17 @@ relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
                                  void* workspace, int64_t workspace_bytes, void* stream) {
   if (workspace_bytes < 0) return RELPOS_E_VALUE;
   return attn_fwd_impl(q, k, v, rel_h, rel_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
-                       true, workspace, workspace_bytes, stream);
+                       true, workspace, workspace_bytes, stream, -1);
+}
+
+relpos_status relpos_attn_fwd_cfg(const void* q, const void* k, const void* v,
+                                  const float* rel_h, const float* rel_w, void* out,
+                                  int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                  float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                  int config, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (workspace_bytes < 0 || (config != -1 && !config_known(config))) return RELPOS_E_VALUE;
+  return attn_fwd_impl(q, k, v, rel_h, rel_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
+                       true, workspace, workspace_bytes, stream, config);
 }
 
 }  // extern "C"

@@ -1,15 +1,14 @@
-// relpos_attn_fwd, 16-query-per-wave kernel (launch configurations 3 and 4).
+// relpos_attn_fwd, 16-query-per-wave kernel (launch configuration 3).
 //
 // Same method as the 32-query kernel in relpos_attn_fwd.hip (PR #55629 page,
 // implementation section, item 1: K/V streamed with an online softmax and the
 // rel_h/rel_w slices added per key block), laid out for more waves per SIMD:
 //
-//   * A wave owns 16 queries; a workgroup of NW waves owns 16*NW queries of one
-//     (batch, head).  With NW = 4 a workgroup covers 64 queries (three per CU
-//     on a 64x64 grid with 12 heads) and three waves fit per SIMD.  Measured on
-//     MI355X it is slower than the 32-query kernel on every workload here (twice
-//     the LDS operand traffic per score, and 16x16 MFMAs hide less VALU work),
-//     so it is not the default.
+//   * A wave owns 16 queries; a workgroup of 4 waves owns 64 queries of one
+//     (batch, head), and three waves fit per SIMD.  Measured on MI355X it is
+//     slower than the 32-query kernel on long key loops (twice the LDS operand
+//     traffic per score, and 16x16 MFMAs hide less VALU work); its shorter
+//     pipeline wins on units of at most four key tiles (small windows).
 //   * S^T = K Q^T on 16x16x32 MFMA.  A lane holds one query (lane%16) and, per
 //     64-key tile of the key grid (4 rows x 16 columns), 16 keys
 //     o = 16*st + 4*g + j (g = lane/16), i.e. grid row st and grid column
@@ -38,8 +37,10 @@ namespace {
 constexpr int kKSlots16 = 2;
 constexpr int kVSlots16 = 3;
 
-template <bool BF16, bool OUT_F32, int NW>
-__global__ __launch_bounds__(NW * 64, NW <= 4 ? 3 : 2) void attn16_kernel(
+constexpr int NW = 4;
+
+template <bool BF16, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
@@ -120,10 +121,15 @@ __global__ __launch_bounds__(NW * 64, NW <= 4 ? 3 : 2) void attn16_kernel(
   };
 
   // ---- bias: rel_w' for the lane's 4 columns of a band, rel_h' per tile ------
-  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + head * W, static_cast<uint32_t>(N) * W * 4);
-  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + head * H, static_cast<uint32_t>(N) * H * 4);
-  const int rw_off = (qi < N ? qi : 0) * W * 4;
-  const int rh_off = (qi < N ? qi : 0) * H * 4;
+  // The unit's own rows only (at most 64 rows of at most 4096 floats, so the
+  // byte range and the offsets stay far inside 32 bits for every grid).
+  const int unit_rows = N - q0 < BM ? N - q0 : BM;
+  const __amdgpu_buffer_rsrc_t rwrs =
+      make_rsrc(rel_w + (head + q0) * W, static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(W) * 4);
+  const __amdgpu_buffer_rsrc_t rhrs =
+      make_rsrc(rel_h + (head + q0) * H, static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(H) * 4);
+  const int rw_off = (qi < N ? qrow : 0) * W * 4;
+  const int rh_off = (qi < N ? qrow : 0) * H * 4;
   float rw[4];
   auto load_band = [&](int kw0) {
 #pragma unroll
@@ -316,9 +322,9 @@ __global__ __launch_bounds__(NW * 64, NW <= 4 ? 3 : 2) void attn16_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32, int NW>
+template <bool BF16, bool OUT_F32>
 hipError_t launch16(const AttnArgs& a, hipStream_t stream) {
-  auto kern = attn16_kernel<BF16, OUT_F32, NW>;
+  auto kern = attn16_kernel<BF16, OUT_F32>;
   const size_t lds = attn16_lds_bytes();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -333,20 +339,15 @@ hipError_t launch16(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool OUT_F32>
-hipError_t launch16_nw(const AttnArgs& a, int nw, hipStream_t stream) {
-  return nw == 8 ? launch16<BF16, OUT_F32, 8>(a, stream) : launch16<BF16, OUT_F32, 4>(a, stream);
-}
-
 }  // namespace
 
 size_t attn16_lds_bytes() { return static_cast<size_t>(kKSlots16 + kVSlots16) * kTileHalves * 2; }
 
-hipError_t launch_attn16(const AttnArgs& a, int nw, hipStream_t stream) {
+hipError_t launch_attn16(const AttnArgs& a, hipStream_t stream) {
   if (a.bf16) {
-    return a.out_f32 ? launch16_nw<true, true>(a, nw, stream) : launch16_nw<true, false>(a, nw, stream);
+    return a.out_f32 ? launch16<true, true>(a, stream) : launch16<true, false>(a, stream);
   }
-  return a.out_f32 ? launch16_nw<false, true>(a, nw, stream) : launch16_nw<false, false>(a, nw, stream);
+  return a.out_f32 ? launch16<false, true>(a, stream) : launch16<false, false>(a, stream);
 }
 
 }  // namespace relpos

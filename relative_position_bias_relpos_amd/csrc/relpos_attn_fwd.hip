@@ -214,7 +214,7 @@ __device__ __forceinline__ void attn_segment(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int q_tiles, float c2, float rw_mul,
+    int H, int W, int q_tiles, float c2, float rw_mul, bool zero_q,
     float* __restrict__ ws, int unit, int t0, int nt, int slot,
     const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw, float* bias_slot) {
   constexpr int BM = 32 * NW;
@@ -356,7 +356,9 @@ __device__ __forceinline__ void attn_segment(
         const int dc = 8 * (i >> 2) + (i & 3);  // column offset beyond 4*half
         const int c = kw0 + dc + 4 * half;
         const float y = buf_loadf(rwrs, c < W ? rw_lane + 4 * (kw0 + dc) : kOob);
-        x[i] = c < W ? y * rw_mul : -__builtin_inff();
+        // The mask is scaled with the values: rw_mul has the sign of the
+        // scale, and the product with c2 below turns it back into -inf.
+        x[i] = (c < W ? y : -__builtin_inff()) * rw_mul;
       }
     }
 #pragma unroll
@@ -484,6 +486,14 @@ __device__ __forceinline__ void attn_segment(
   acc[1] = f32x16{};
   float m = 0.f, l = 0.f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  // scale == 0: the scores are the bias alone.  The launch then passes c2 =
+  // log2(e) and rw_mul = 1 and the q.k products are taken against zero Q
+  // fragments (after the fused bias rows, which need the real q).
+  if (zero_q) {
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) qf[kd] = u32x4{0, 0, 0, 0};
+  }
 
   f32x16 sA[2], sB[2];
   u32x4 pA[4], pB[4];
@@ -750,7 +760,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int q_tiles, float c2, float rw_mul,
+    int H, int W, int q_tiles, float c2, float rw_mul, int zero_q,
     float* __restrict__ ws, SplitPlan plan,
     const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw) {
   static_assert(!FUSED || SPLIT, "the fused bias needs the persistent grid");
@@ -764,25 +774,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_kernel(
   }
   if constexpr (!SPLIT) {
     attn_segment<BF16, OUT_F32, NW, ALIGNED, false, false, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
-                                                           rw_mul, ws, L, 0, T, 0, th, tw, bias_slot);
+                                                           rw_mul, zero_q != 0, ws, L, 0, T, 0, th, tw, bias_slot);
   } else {
     const int P = static_cast<int>(gridDim.x);
     for (int i = 0; i < plan.rounds; ++i) {
       attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
-                                                            rw_mul, ws, i * P + L, 0, T, 0, th, tw, bias_slot);
+                                                            rw_mul, zero_q != 0, ws, i * P + L, 0, T, 0, th, tw, bias_slot);
       __syncthreads();  // the next segment reuses the LDS ring
     }
     const int base = plan.rounds * P;
     if (L < plan.rest) {
       attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
-                                                            rw_mul, ws, base + L, 0, plan.s, 2 * L, th, tw,
+                                                            rw_mul, zero_q != 0, ws, base + L, 0, plan.s, 2 * L, th, tw,
                                                             bias_slot);
     } else if (plan.s < T) {
       for (int j = 0; j < plan.k; ++j) {
         const int ui = (L - plan.rest) * plan.k + j;
         if (ui >= plan.rest) break;
         attn_segment<BF16, OUT_F32, NW, ALIGNED, true, FUSED, RH_LDS>(q, k, v, rel_h, rel_w, out, H, W, q_tiles, c2,
-                                                              rw_mul, ws, base + ui, plan.s, T - plan.s,
+                                                              rw_mul, zero_q != 0, ws, base + ui, plan.s, T - plan.s,
                                                               2 * ui + 1, th, tw, bias_slot);
         __syncthreads();
       }
@@ -821,11 +831,17 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
     }
     grid = static_cast<unsigned>(a.split_ctas);
   }
-  const float c2 = a.scale * kLog2e;
+  // Scores are s * c2 + rel_h * log2(e) - m with s = q.k + rel_w * rw_mul
+  // (rel_w enters through the MFMA accumulator), so rw_mul = log2(e) / c2.
+  // scale == 0 has no such fold: Q is zeroed in the kernel instead, and s =
+  // rel_w times c2 = log2(e) gives the bias alone.
+  const bool zero_q = a.scale == 0.0f;
+  const float c2 = zero_q ? kLog2e : a.scale * kLog2e;
+  const float rw_mul = zero_q ? 1.0f : kLog2e / c2;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, q_tiles, c2, kLog2e / c2, ws, plan,
+                     a.H, a.W, q_tiles, c2, rw_mul, zero_q ? 1 : 0, ws, plan,
                      static_cast<const uint16_t*>(a.th), static_cast<const uint16_t*>(a.tw));
   if constexpr (SPLIT) {
     if (plan.rest > 0 && plan.s < T) {
@@ -859,7 +875,6 @@ hipError_t launch_dt(const AttnArgs& a, int cfg, hipStream_t stream) {
   switch (cfg) {
     case 0: return launch_nw<BF16, OUT_F32, 8, false>(a, stream);
     case 1: return launch_nw<BF16, OUT_F32, 4, false>(a, stream);
-    case 2: return launch_nw<BF16, OUT_F32, 2, false>(a, stream);
     default: return launch_nw<BF16, OUT_F32, 8, true>(a, stream);  // kAttnSplitConfig
   }
 }
@@ -867,8 +882,6 @@ hipError_t launch_dt(const AttnArgs& a, int cfg, hipStream_t stream) {
 
 
 }  // namespace
-
-int attn_num_configs() { return 6; }
 
 size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas) {
   (void)BH;
@@ -903,15 +916,13 @@ size_t attn_lds_bytes(int cfg, int H, int W) {
   (void)W;
   switch (cfg) {
     case 1: return attn32_lds_bytes<4>();
-    case 2: return attn32_lds_bytes<2>();
-    case 3:
-    case 4: return attn16_lds_bytes();
+    case 3: return attn16_lds_bytes();
     default: return attn32_lds_bytes<8>();  // 0 and kAttnSplitConfig
   }
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
-  if (cfg == 3 || cfg == 4) return launch_attn16(a, cfg == 3 ? 4 : 8, stream);
+  if (cfg == 3) return launch_attn16(a, stream);
   if (a.bf16) {
     return a.out_f32 ? launch_dt<true, true>(a, cfg, stream) : launch_dt<true, false>(a, cfg, stream);
   }

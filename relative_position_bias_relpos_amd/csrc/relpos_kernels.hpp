@@ -47,10 +47,9 @@ struct AttnArgs {
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
 // Attention launch configurations:
-//   0, 1, 2: 32 queries per wave, 8, 4 or 2 waves per workgroup, one
-//            workgroup per unit of 32*waves queries
+//   0, 1: 32 queries per wave, 8 or 4 waves per workgroup, one workgroup
+//         per unit of 32*waves queries
 //   3: 16 queries per wave, 4 waves per workgroup (64 queries)
-//   4: 16 queries per wave, 8 waves per workgroup (128 queries)
 //   5: configuration 0 with the key range split over a persistent grid of
 //      split_ctas workgroups (needs the workspace)
 constexpr int kAttnSplitConfig = 5;
@@ -99,7 +98,6 @@ inline SplitPlan split_plan(int64_t units, int T, int P, int pro = 0) {
   if (p.s > T - 1) p.s = T < 2 ? T : T - 1;
   return p;
 }
-int attn_num_configs();
 size_t attn_split_workspace_bytes(int64_t BH, int64_t N, int ctas);
 // The fused path: configuration kAttnSplitConfig's kernel with the bias
 // computed in the kernel.  Workspace: the split pieces, then one slot of bias
@@ -112,6 +110,6 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
 
 // The 16-query-per-wave kernel (relpos_attn16.hip).
 size_t attn16_lds_bytes();
-hipError_t launch_attn16(const AttnArgs& a, int nw, hipStream_t stream);
+hipError_t launch_attn16(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace relpos

@@ -20,12 +20,24 @@ def to_dev(d):
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
 
-def gpu_run(d, out_dtype=torch.float32):
-    """relpos_build then relpos_attn_fwd on torch's current stream; synchronised."""
+def cu_count():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def split_ws_bytes():
+    """The workspace size include/relpos.h documents for the split launch."""
+    return cu_count() * 2 * (256 * 64 + 2 * 256) * 4
+
+
+def gpu_run(d, out_dtype=torch.float32, config=None, workspace=None):
+    """relpos_build then relpos_attn_fwd on torch's current stream; synchronised.
+    config / workspace as in the binding (None: the library's own choice)."""
     g = to_dev(d)
     rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
+    if config == 5 and workspace is None:
+        workspace = torch.empty(split_ws_bytes(), dtype=torch.uint8, device="cuda")
     out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"],
-                             out_dtype=out_dtype)
+                             out_dtype=out_dtype, config=config, workspace=workspace)
     torch.cuda.synchronize()
     return out, rel_h, rel_w
 
@@ -33,6 +45,27 @@ def gpu_run(d, out_dtype=torch.float32):
 def oracle_full(d):
     return O.relpos_attention(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(d["rel_pos_h"]),
                               f64(d["rel_pos_w"]), d["H"], d["W"], d["scale"])
+
+
+def oracle_out_parallel(d, workers=4):
+    """The oracle's output for every (batch, head), heads spread over a few
+    threads (numpy releases the GIL in its array work); each head is one plain
+    call of the oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+    q, k, v = d["q"], d["k"], d["v"]
+    th, tw = f64(d["rel_pos_h"]), f64(d["rel_pos_w"])
+    B, nh, N, D = q.shape
+    out = np.empty((B, nh, N, D), dtype=np.float64)
+
+    def one(bh):
+        b, h = divmod(bh, nh)
+        o, _, _ = O.relpos_attention(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]), f64(v[b:b + 1, h:h + 1]),
+                                     th, tw, d["H"], d["W"], d["scale"])
+        out[b, h] = o[0, 0]
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(B * nh)))
+    return out
 
 
 def sample_rows(N, n, seed, H, W):

@@ -43,7 +43,7 @@ def lib():
 def test_header_declares_the_calls():
     names = set(_declared())
     assert {"relpos_build", "relpos_attn_fwd", "relpos_attn_fwd_ws", "relpos_attn_workspace_bytes",
-            "relpos_attn_config", "relpos_status_string", "relpos_abi_version"} <= names
+            "relpos_attn_config", "relpos_attn_fwd_cfg", "relpos_status_string", "relpos_abi_version"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -103,6 +103,37 @@ def test_dtype_errors(lib):
 def test_scale_must_be_finite(lib):
     assert attn(lib, scale=float("nan")) == E_VALUE
     assert attn(lib, scale=float("inf")) == E_VALUE
+
+
+def test_scale_rule(lib):
+    """0 and any |scale| >= 2^-64 pass the scalar check (the call then stops at
+    the misaligned pointer); 0 < |scale| < 2^-64 is E_VALUE."""
+    bad = [x + 2 for x in P]
+    for scale in (0.0, -0.0, -0.125, 2.0 ** -64, -(2.0 ** -64), 1e30):
+        assert attn(lib, ptrs=bad, scale=scale) == E_ALIGN, scale
+        assert _fused(lib, ptrs=bad + [0x10000 * 7 + 2], scale=scale) == E_ALIGN, scale
+    for scale in (2.0 ** -65, -(2.0 ** -70), 1e-30, 1e-45):
+        assert attn(lib, ptrs=bad, scale=scale) == E_VALUE, scale
+        assert _fused(lib, ptrs=bad + [0x10000 * 7 + 2], scale=scale) == E_VALUE, scale
+
+
+def _cfg_call(lib, config, ptrs=None, ws=0, ws_bytes=0, D=64, scale=0.125):
+    f = lib.relpos_attn_fwd_cfg
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    p = ptrs or P
+    return f(*[vp(x) for x in p], 1, 2, 4, 4, D, scale, BF16, FP32, config, vp(ws), ws_bytes, vp(0))
+
+
+def test_attn_fwd_cfg_argument_checks(lib):
+    bad = [x + 2 for x in P]
+    for config in (-1, 0, 1, 3, 5):  # known configurations reach the pointer checks
+        assert _cfg_call(lib, config, ptrs=bad) == E_ALIGN, config
+    for config in (-2, 2, 4, 7, 1000):
+        assert _cfg_call(lib, config, ptrs=bad) == E_VALUE, config
+    assert _cfg_call(lib, 0, ptrs=bad, ws_bytes=-1) == E_VALUE
+    assert _cfg_call(lib, 0, D=32) == E_SHAPE
 
 
 def test_empty_batch_is_a_noop(lib):

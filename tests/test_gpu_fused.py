@@ -85,18 +85,6 @@ def test_small_grids_full(name, kw):
     _check(f"{name} {kw}", np.abs(G.f64(_fused(d)) - ref))
 
 
-@pytest.mark.parametrize("name,rows", [("deepencoder", 96), ("batched_fp16", 48), ("rect", 48), ("vitl", 32)])
-def test_full_size_sampled(name, rows):
-    d = G.make(name)
-    print(f"[fused] full {name}", flush=True)
-    out = _fused(d)
-    _check(f"{name} sampled", G.oracle_sampled(d, out, rows))
-    # Same operation as the two-call path; the two differ by rounding only.
-    two, _, _ = G.gpu_run(d)
-    assert (out - two).abs().max().item() <= G.MAX_ABS
-    assert torch.equal(out, _fused(d)), "not reproducible run to run"
-
-
 def test_ones_v_gives_ones():
     d = G.make("rect", B=1, heads=2, H=24, W=40)
     d["v"] = torch.ones_like(d["v"])

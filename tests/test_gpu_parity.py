@@ -1,11 +1,10 @@
 """Parity of the HIP path (through the C ABI) against the float64 oracle.
 
 Bar: max |gpu - oracle| <= 2e-3 and mean <= 1e-4 on the attention output (fp32
-out); rel_h/rel_w within the fp32 dot-product forward-error bound.  Small grids
-are compared element by element over every output; the full-size workloads run
-in the benchmarked launch configuration and are compared on sampled query rows
-(every head, random rows plus tile/grid boundary rows), which the oracle
-computes one by one.
+out); rel_h/rel_w within the fp32 dot-product forward-error bound.  Small and
+ragged grids are compared element by element over every output, in every
+launch configuration; the full-size workloads are compared over every output
+in tests/test_gpu_full_parity.py.
 """
 
 import gc
@@ -77,17 +76,6 @@ def test_small_stress_fp16_full():
     _check("stress fp16 12x20", np.abs(G.f64(out) - ref))
 
 
-# ---- attention at full size, sampled rows -----------------------------------
-
-@pytest.mark.parametrize("name,rows", [("deepencoder", 160), ("batched_fp16", 64), ("rect", 64), ("vitl", 48)])
-def test_full_size_sampled(name, rows):
-    d = G.make(name)
-    print(f"[full] {name}", flush=True)
-    out, _, _ = G.gpu_run(d)
-    err = G.oracle_sampled(d, out, rows)
-    _check(f"{name} sampled", err)
-
-
 # ---- properties on the GPU ---------------------------------------------------
 
 def test_ones_v_gives_ones():
@@ -156,46 +144,37 @@ def test_no_allocation_during_calls():
 
 # ---- every launch configuration ------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 3, 5])
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("rect", dict(B=1, heads=2, H=21, W=35)),
                                      ("batched_fp16", dict(B=1, heads=2, H=20, W=24))])
-def test_each_launch_config(cfg, name, kw, monkeypatch):
-    monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
+def test_each_launch_config(cfg, name, kw):
     d = G.make(name, **kw)
-    out, _, _ = G.gpu_run(d)
+    out, _, _ = G.gpu_run(d, config=cfg)
     ref, _, _ = G.oracle_full(d)
     _check(f"cfg{cfg} {name}", np.abs(G.f64(out) - ref))
 
 
 @pytest.mark.parametrize("name", ["deepencoder", "rect", "batched_fp16", "windowed"])
-def test_automatic_config_matches_its_prediction(name, monkeypatch):
-    """Without RELPOS_ATTN_CFG the library launches the configuration that
-    relpos_attn_config predicts for this device: same bits as forcing it."""
+def test_automatic_config_matches_its_prediction(name):
+    """relpos_attn_fwd launches the configuration relpos_attn_config predicts
+    for this device: the same bits as forcing it through relpos_attn_fwd_cfg."""
     from relative_position_bias_relpos_amd import binding as rp
-    d = G.make(name)  # full size: configuration 0 for the 64x64 grids, 1 for 48x80, 3 for the windows
-    monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
+    d = G.make(name)
     auto, _, _ = G.gpu_run(d)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, nh = d["q"].shape[:2]
-    cfg = rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, cus)
-    monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
-    forced, _, _ = G.gpu_run(d)
+    cfg = rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, G.cu_count())
+    forced, _, _ = G.gpu_run(d, config=cfg)
     assert torch.equal(auto, forced), (name, cfg)
 
 
 # ---- key-range split (relpos_attn_fwd_ws) ----------------------------------------
 
-def _split_ws_bytes():
-    """The workspace size documented in include/relpos.h for the split launch."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return cus * 2 * (256 * 64 + 2 * 256) * 4
-
-
-def _run_split(d, ws):
+def _run_split(d, ws, config=None):
     from relative_position_bias_relpos_amd import binding as rp
     g = G.to_dev(d)
     rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
-    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=ws)
+    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=ws,
+                             config=config)
     torch.cuda.synchronize()
     return out
 
@@ -203,48 +182,33 @@ def _run_split(d, ws):
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("tiny", dict(H=14, W=14)), ("tiny", dict(H=7, W=9, dtype="fp16")),
                                      ("rect", dict(B=1, heads=3, H=21, W=35)),
                                      ("batched_fp16", dict(B=1, heads=2, H=20, W=24))])
-def test_forced_split_full(name, kw, monkeypatch):
+def test_forced_split_full(name, kw):
     """Forced split on small grids: every unit is in the last round, cut into a
     head and a tail (down to one tile each) that are merged afterwards."""
-    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
     d = G.make(name, **kw)
-    ws = torch.full((_split_ws_bytes(),), 0x7f, dtype=torch.uint8, device="cuda")  # contents are not read
-    out = _run_split(d, ws)
+    ws = torch.full((G.split_ws_bytes(),), 0x7f, dtype=torch.uint8, device="cuda")  # contents are not read
+    out = _run_split(d, ws, config=5)
     ref, _, _ = G.oracle_full(d)
     _check(f"split {name} {kw}", np.abs(G.f64(out) - ref))
-    again = _run_split(d, ws)
+    again = _run_split(d, ws, config=5)
     assert torch.equal(out, again), "split result depends on arrival order"
 
 
-@pytest.mark.parametrize("name,rows", [("deepencoder", 96), ("rect", 48), ("vitl", 32)])
-def test_split_full_size_sampled(name, rows, monkeypatch):
-    """The split launch on the full-size workloads: chosen by the cost model
-    for 96x96 (checked here) and 48x80, forced for 64x64 (where the unsplit
-    launch is chosen)."""
+def test_split_chosen_with_a_workspace():
+    """relpos_attn_fwd_ws with a workspace splits the 96x96 workload (the cost
+    model's choice there) and asks for the documented workspace size."""
     from relative_position_bias_relpos_amd import binding as rp
-    d = G.make(name)
+    d = G.make("vitl")
     B, nh = d["q"].shape[:2]
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if name == "vitl":
-        monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
-        assert rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, cus) == 5
-        assert rp.workspace_bytes(B, nh, d["H"], d["W"], d["q"].dtype, cus) == _split_ws_bytes()
-    else:
-        monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
-    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda")
+    assert rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, G.cu_count(), with_workspace=True) == 5
+    assert rp.workspace_bytes(B, nh, d["H"], d["W"], d["q"].dtype, G.cu_count()) == G.split_ws_bytes()
+    ws = torch.empty(G.split_ws_bytes(), dtype=torch.uint8, device="cuda")
     out = _run_split(d, ws)
-    _check(f"{name} split sampled", G.oracle_sampled(d, out, rows))
-    # Each piece rounds p to fp16 against its own reference maximum, so the
-    # split and unsplit launches differ by rounding only (both meet the bar).
-    unsplit = _run_split(d, None)
-    assert (out - unsplit).abs().max().item() <= G.MAX_ABS
-    for _ in range(2):
-        assert torch.equal(out, _run_split(d, ws))
+    assert torch.equal(out, _run_split(d, ws, config=5))
 
 
-def test_split_workspace_errors(monkeypatch):
+def test_split_workspace_errors():
     from relative_position_bias_relpos_amd import binding as rp
-    monkeypatch.delenv("RELPOS_ATTN_CFG", raising=False)
     d = G.make("vitl", B=1)  # 16 heads of 96x96: the cost model splits it
     g = G.to_dev(d)
     rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
@@ -252,52 +216,46 @@ def test_split_workspace_errors(monkeypatch):
     with pytest.raises(rp.RelposError) as e:
         rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=small)
     assert e.value.status == 2  # E_SHAPE: workspace too small
-    big = torch.zeros(_split_ws_bytes() + g["q"].numel() * 4, dtype=torch.uint8, device="cuda")
+    big = torch.zeros(G.split_ws_bytes() + g["q"].numel() * 4, dtype=torch.uint8, device="cuda")
     out = big[: g["q"].numel() * 4].view(torch.float32).view(g["q"].shape)
     with pytest.raises(rp.RelposError) as e:
         rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], out=out, workspace=big)
     assert e.value.status == 6  # E_ALIAS: the workspace overlaps out
+    with pytest.raises(rp.RelposError) as e:
+        rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], config=5)
+    assert e.value.status == 1  # E_NULL: the forced split without a workspace
 
 
-def test_split_workspace_reused_across_shapes(monkeypatch):
+def test_split_workspace_reused_across_shapes():
     """One workspace for split problems of different shapes in turn."""
-    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
-    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(G.split_ws_bytes(), dtype=torch.uint8, device="cuda")
     for d in (G.make("deepencoder", B=1, heads=2), G.make("rect", B=1, heads=6), G.make("deepencoder", B=1, heads=2)):
-        out = _run_split(d, ws)
+        out = _run_split(d, ws, config=5)
         unsplit = _run_split(d, None)
         assert (out - unsplit).abs().max().item() <= G.MAX_ABS
-        assert torch.equal(out, _run_split(d, ws))
+        assert torch.equal(out, _run_split(d, ws, config=5))
 
 
 @pytest.mark.parametrize("cfg", [0, 5])
 @pytest.mark.parametrize("H,W", [(12, 32), (72, 16), (76, 16)])
-def test_rel_h_rows_in_lds_shapes(cfg, H, W, monkeypatch):
+def test_rel_h_rows_in_lds_shapes(cfg, H, W):
     """8-wave launches copy each unit's rel_h rows to LDS on tile-aligned grids
     with H <= 72: a last unit whose upper waves lie past the grid (12x32: 384
     queries), the largest H of that path (72: nine 16-byte chunks per lane, and
     a half-empty last unit) and the first H past it (76: rel_h read from memory)."""
-    monkeypatch.setenv("RELPOS_ATTN_CFG", str(cfg))
     d = G.make("tiny", H=H, W=W)
-    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda") if cfg == 5 else None
-    out = _run_split(d, ws)
+    ws = torch.empty(G.split_ws_bytes(), dtype=torch.uint8, device="cuda") if cfg == 5 else None
+    out = _run_split(d, ws, config=cfg)
     ref, _, _ = G.oracle_full(d)
     _check(f"cfg{cfg} rel_h rows {H}x{W}", np.abs(G.f64(out) - ref))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_forced_split_half_precision_output(dtype, monkeypatch):
+def test_forced_split_half_precision_output(dtype):
     """The merge kernel's bf16/fp16 stores, against the oracle."""
-    from relative_position_bias_relpos_amd import binding as rp
-    monkeypatch.setenv("RELPOS_ATTN_CFG", "5")
     d = G.make("tiny", dtype=dtype, H=14, W=18)
-    g = G.to_dev(d)
-    rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
-    ws = torch.empty(_split_ws_bytes(), dtype=torch.uint8, device="cuda")
-    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"],
-                             out_dtype=g["q"].dtype, workspace=ws)
-    torch.cuda.synchronize()
-    assert out.dtype == g["q"].dtype
+    out, _, _ = G.gpu_run(d, out_dtype=d["q"].dtype, config=5)
+    assert out.dtype == d["q"].dtype
     ref, _, _ = G.oracle_full(d)
     err = np.abs(G.f64(out) - ref)
     ulp = 2.0 ** (-8 if dtype == "bf16" else -11)

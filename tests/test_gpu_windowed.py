@@ -37,7 +37,10 @@ def test_two_call_path_with_workspace(case):
     d, ref = case
     g = G.to_dev(d)
     rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
-    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace="auto")
+    B, nh = g["q"].shape[:2]
+    n = max(rp.workspace_bytes(B, nh, d["H"], d["W"], g["q"].dtype, G.cu_count()), 16)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = rp.relpos_attn_fwd(g["q"], g["k"], g["v"], rel_h, rel_w, d["H"], d["W"], d["scale"], workspace=ws)
     torch.cuda.synchronize()
     _check("build + attn_fwd_ws", np.abs(G.f64(out) - ref))
 
