@@ -134,37 +134,84 @@ def dense_sdpa_context(w, q, k, v, rel_h, rel_w, ours, out, rounds=3):
         return {"kind": "context: dense bias + torch SDPA", "unavailable": f"{type(e).__name__}: {e}"[:200]}
 
 
-def gpu_clocks(dev_index=0):
-    """Current graphics and memory clocks (MHz) of the GPU torch uses, from
-    amdsmi; None where the query is not available."""
-    try:
-        import amdsmi
-        import torch
+class ClockSampler:
+    """Polls the graphics and memory clocks (MHz) of the GPU torch uses, from
+    amdsmi, in a background thread while the GPU works; reports the samples'
+    median, min and max per phase.  Best effort: where amdsmi is missing or
+    not permitted, it reports why and the bench goes on."""
 
-        amdsmi.amdsmi_init()
+    def __init__(self, dev_index=0, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.samples = {}
+        self.phase = None
+        self.error = None
+        self._stop = threading.Event()
+        self._lock = threading.Lock()
+        self.handle = None
         try:
+            import amdsmi
+            import torch
+
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
             handles = amdsmi.amdsmi_get_processor_handles()
-            handle = handles[0] if handles else None
-            props = torch.cuda.get_device_properties(dev_index)
-            want = getattr(props, "pci_bus_id", None)
+            self.handle = handles[0] if handles else None
+            want = getattr(torch.cuda.get_device_properties(dev_index), "pci_bus_id", None)
             for h in handles:
                 try:
-                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
-                    if want is not None and int(bdf.split(":")[1], 16) == int(want):
-                        handle = h
+                    if want is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == int(want):
+                        self.handle = h
                         break
                 except Exception:
                     pass
-            if handle is None:
-                return None
-            g = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
-            m = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.MEM)
-            return {"sclk_mhz": g.get("clk"), "sclk_max_mhz": g.get("max_clk"),
-                    "mclk_mhz": m.get("clk"), "mclk_max_mhz": m.get("max_clk")}
-        finally:
-            amdsmi.amdsmi_shut_down()
-    except Exception as e:  # no amdsmi, or no permission: report, never fail the bench
-        return {"unavailable": f"{type(e).__name__}: {e}"[:120]}
+            self.read()
+        except Exception as e:
+            self.error = f"{type(e).__name__}: {e}"[:120]
+            self.handle = None
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def read(self):
+        g = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
+        m = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.MEM)
+        return g.get("clk"), m.get("clk"), g.get("max_clk")
+
+    def _run(self):
+        while not self._stop.is_set():
+            if self.handle is not None and self.phase is not None:
+                try:
+                    sclk, mclk, smax = self.read()
+                    with self._lock:
+                        self.samples.setdefault(self.phase, []).append((sclk, mclk))
+                        self.sclk_max = smax
+                except Exception as e:
+                    self.error = f"{type(e).__name__}: {e}"[:120]
+            time.sleep(self.period)
+
+    def set_phase(self, name):
+        with self._lock:
+            self.phase = name
+
+    def report(self):
+        import statistics
+        self._stop.set()
+        self._thread.join(timeout=1.0)
+        try:
+            if self.handle is not None:
+                self.amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        if self.handle is None:
+            return {"unavailable": self.error}
+        out = {"sclk_max_mhz": getattr(self, "sclk_max", None), "period_ms": self.period * 1e3}
+        for ph, xs in self.samples.items():
+            sc = [x[0] for x in xs if x[0] is not None]
+            mc = [x[1] for x in xs if x[1] is not None]
+            if sc:
+                out[ph] = {"n": len(sc), "sclk_median_mhz": statistics.median(sc), "sclk_min_mhz": min(sc),
+                           "sclk_max_mhz": max(sc), "mclk_median_mhz": statistics.median(mc) if mc else None}
+        return out
 
 
 def rocm_version():
@@ -261,7 +308,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    clocks_idle = gpu_clocks()
+    clk = ClockSampler()
+    clk.set_phase("settle")
     # Clock settle: back-to-back steps (and fused calls) for --settle-ms of wall
     # time, synchronised every 20 so the queue stays short.
     settle_calls = 0
@@ -277,7 +325,7 @@ def main():
         fused()
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
-    clocks_before = gpu_clocks()
+    clk.set_phase("timed")
 
     # Timed region: exactly K steps bracketed by synchronisations; HIP events
     # on the launch stream (torch's current stream, which the binding passes)
@@ -295,7 +343,7 @@ def main():
     ms_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     build_calls = [e[0].elapsed_time(e[1]) for e in ev]
     attn_calls = [e[1].elapsed_time(e[2]) for e in ev]
-    clocks_after = gpu_clocks()
+    clk.set_phase(None)
 
     # The fused call, timed the same way in its own loop.
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
@@ -377,7 +425,7 @@ def main():
                   "ms_per_step = first event to last / steps; *_ms_per_call = mean of the per-call events",
         "settle": {"ms": args.settle_ms, "calls": settle_calls,
                    "what": "untimed back-to-back steps and fused calls before the warm-up (clock ramp)"},
-        "clocks": {"idle_before_settle": clocks_idle, "before_timed": clocks_before, "after_timed": clocks_after},
+        "clocks": clk.report(),
         "rocm": rocm_version(),
         "torch_hip": torch.version.hip,
         "host_us_per_attn_call": {"python_binding": round(host_us, 2), "c_call_only": round(c_us, 2)},

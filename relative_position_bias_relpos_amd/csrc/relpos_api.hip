@@ -178,7 +178,9 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
 // not fit the device's LDS.
 constexpr int kAttnFallback[] = {0, 1, 3};
 
-bool config_known(int c) { return c == 0 || c == 1 || c == 3 || c == relpos::kAttnSplitConfig; }
+bool config_known(int c) {
+  return c == 0 || c == 1 || c == 3 || c == relpos::kAttnSplitConfig || c == relpos::kAttn12Config;
+}
 
 // Shared body of relpos_attn_fwd, relpos_attn_fwd_ws and relpos_attn_fwd_cfg
 // (forced >= 0: that configuration, which must fit the device's LDS).
@@ -213,6 +215,7 @@ relpos_status attn_fwd_impl(const void* q, const void* k, const void* v,
   DeviceProps props{};
   if (device_props(&props) != 0) return RELPOS_E_HIP;
   auto fits = [&](int c) {
+    if (c == relpos::kAttn12Config && !relpos::attn12_fits(static_cast<int>(H), static_cast<int>(W))) return false;
     return relpos::attn_lds_bytes(c, static_cast<int>(H), static_cast<int>(W)) <=
            static_cast<size_t>(props.lds_limit);
   };

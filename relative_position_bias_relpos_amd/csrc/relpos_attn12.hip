@@ -1,0 +1,565 @@
+// relpos_attn_fwd, 12-wave kernel (launch configuration 6).
+//
+// Same method as the 32-query kernel in relpos_attn_fwd.hip (PR #55629 page,
+// implementation section, item 1: K/V streamed with an online softmax, the
+// rel_h/rel_w slices added per key block, no dense [N, N] bias), with the work
+// cut so that every SIMD of every compute unit gets the same share:
+//
+//   * A workgroup owns 6 query blocks of 32 consecutive queries (192 queries;
+//     block b of the workgroup is global block 6*unit + b in (b*heads,
+//     query) order, so a workgroup may span the end of one head and the start
+//     of the next).  Each block is worked by two waves: the even one takes the
+//     even key tiles, the odd one the odd tiles.  12 waves, three per SIMD.
+//     On the 64x64 grid with 12 heads that is 256 workgroups, one per CU.
+//   * The two waves of a block keep their own online-softmax state (O, m, l)
+//     and merge through LDS at the end; each writes half of the block's
+//     output columns.  No workspace.
+//   * Per step the workgroup stages one tile pair (the next even and odd tile)
+//     per head it spans: K by LDS-direct 16-byte buffer loads (no registers),
+//     V through registers (bf16 is converted to fp16 on the way, so that P.V
+//     runs on fp16 MFMA with fp16 P).  Two LDS slots (step t reads slot t%2
+//     while step t+1's pair is written to the other); V's global loads run one
+//     step ahead.  Tiles are unpadded (8 KB) with XOR-swizzled 16-byte chunks
+//     so the MFMA operand reads hit every LDS bank once.
+//   * Inside a wave a step is plain: S^T = K Q^T (32x32x16 MFMA, rel_w in the
+//     accumulator's initial value), exp2 softmax with a lazy reference maximum,
+//     O^T += V^T P^T.  The three waves of a SIMD overlap one another's MFMA
+//     and VALU work.
+//
+// Lane layouts (S, P, the V transpose read) are the 32-query kernel's; only
+// the LDS addressing differs (swizzle instead of padding).
+#include <type_traits>
+
+#include "relpos_attn_common.hpp"
+#include "relpos_kernels.hpp"
+
+namespace relpos {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kBlocks12 = 6;                       // query blocks per workgroup
+constexpr int kWaves12 = 2 * kBlocks12;            // even and odd tile waves
+constexpr int kThreads12 = 64 * kWaves12;
+constexpr int kTileBytes12 = kTileKeys * kD * 2;   // one K or V tile, 8 KB
+constexpr int kPairBytes12 = 4 * kTileBytes12;     // K even, K odd, V even, V odd
+constexpr int kSlotBytes12 = 2 * kPairBytes12;     // one pair per head spanned
+constexpr int kRawBytes12 = 2 * 2 * kTileBytes12;   // V of a pair as loaded, per head (before conversion)
+constexpr int kLds12 = 2 * kSlotBytes12 + kRawBytes12;  // two slots + the raw V area: 160 KB
+constexpr int kMergeStride12 = 64 * 16 * 4 + 2 * 32 * 4;  // per wave: 16 accumulators per lane, m, l
+
+// Byte offset of K chunk c (16 bytes, d = 8c .. 8c+7) of tile row o: rows of
+// 128 bytes, chunk index XOR-ed with bits 1..3 of the row, so that the 16
+// rows a 16-lane group of the Q.K^T operand read touches fall on 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int k_off(int o, int c) { return o * 128 + 16 * (c ^ ((o >> 1) & 7)); }
+// Byte offset of V chunk c of row o: 8-byte units XOR-ed with 8 * bit 1 of
+// the row, so that the four rows of a transpose-read lane group and the two
+// groups of a 32-lane pass cover the 64 banks once.
+__device__ __forceinline__ int v_off(int o, int c) { return o * 128 + 16 * (c ^ (4 * ((o >> 1) & 1))); }
+
+typedef uint32_t __attribute__((ext_vector_type(4))) sgpr4;
+
+// Raw buffer descriptor words (base, no stride, `bytes` records, raw-buffer
+// flags) for the LDS-direct load below; wave-uniform.
+__device__ __forceinline__ sgpr4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32))) & 0xffffu;
+  return sgpr4{lo, hi, bytes, kBufFlags};
+}
+
+// One LDS-direct 16-byte buffer load per lane: lane L's 16 bytes at byte
+// offset voff + soff of the buffer land at LDS byte lds + 16*L (offsets past
+// the buffer's size read zeros).  Written as asm because the compiler, which
+// cannot tell LDS written this way from the LDS other instructions read,
+// otherwise waits for every outstanding vector load before each LDS read and
+// barrier that follows.  Nothing is returned in registers: the data is only
+// read after this wave's explicit vmcnt(0) wait and a workgroup barrier.
+__device__ __forceinline__ void lds_load16(sgpr4 rs, int voff, int soff, uint32_t lds) {
+  __asm__ volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
+
+template <bool BF16, bool OUT_F32, bool ALIGNED>
+__global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
+    const float* __restrict__ rel_w, void* __restrict__ out,
+    int H, int W, int nblk, int total_blocks, float c2, float rw_mul, int zero_q) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int N = H * W;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int blk = wave >> 1, par = wave & 1;
+
+  // ---- this workgroup's blocks and heads -------------------------------------
+  const int unit = xcd_work_index(static_cast<int>(gridDim.x));
+  const int gb0 = unit * kBlocks12;
+  const int gb_last = gb0 + kBlocks12 - 1 < total_blocks - 1 ? gb0 + kBlocks12 - 1 : total_blocks - 1;
+  const int bhA = gb0 / nblk;
+  const bool two = gb_last / nblk != bhA;  // the workgroup spans two heads
+  const bool bvalid = gb0 + blk < total_blocks;
+  const int gb = bvalid ? gb0 + blk : total_blocks - 1;
+  const int bh = gb / nblk;
+  const int q0 = (gb - bh * nblk) * 32;
+  const int hs = bh - bhA;  // head slot of this wave's block
+  const size_t head = static_cast<size_t>(bh) * N;
+
+  const int band_tiles = (H + kTileRows - 1) / kTileRows;
+  const int T = band_tiles * ((W + kTileCols - 1) / kTileCols);
+  const int steps = (T + 1) / 2;
+
+  // ---- Q^T operand fragments of this wave's 32 queries -----------------------
+  const int ql = lane & 31;
+  const int qi = q0 + ql;
+  const bool qok = qi < N;
+  u32x4 qf[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) {
+    qf[kd] = (qok && zero_q == 0) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
+                                  : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- staging ------------------------------------------------------------------
+  // Every load is an LDS-direct 16-byte buffer load: waves 0..7 bring in V
+  // (2 of a pair's 16 1-KB row blocks each, per head spanned), waves 8..11 K
+  // (4 row blocks each).
+  const bool v_wave = wave < 8;
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
+  const sgpr4 krs0 = rsrc_words(k + static_cast<size_t>(bhA) * N * kD, head_bytes);
+  const sgpr4 krs1 = rsrc_words(k + static_cast<size_t>(bhA + 1) * N * kD, head_bytes);
+  const sgpr4 vrs0 = rsrc_words(v + static_cast<size_t>(bhA) * N * kD, head_bytes);
+  const sgpr4 vrs1 = rsrc_words(v + static_cast<size_t>(bhA + 1) * N * kD, head_bytes);
+
+  // V: wave w < 8 loads row blocks rb = 2*(w&3) + j (j = 0, 1) of tile w>>2
+  // of a pair into the raw area (lane L: row 8*rb + L/8, chunk L%8, as in
+  // memory), and at the end of the step converts exactly those 16 bytes per
+  // lane (bf16 -> fp16) into the slot's swizzled V tile.  No barrier is
+  // needed between the two: each lane reads back what its own load wrote,
+  // after waiting for it.
+  const int v_tile = (wave >> 2) & 1;
+  int v_goff[2], v_lds[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int o = 8 * (2 * (wave & 3) + j) + (lane >> 3);
+    v_goff[j] = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * (lane & 7);
+    v_lds[j] = (2 + v_tile) * kTileBytes12 + v_off(o, lane & 7);
+  }
+  unsigned char* raw = smem + 2 * kSlotBytes12;
+  auto raw_off = [&](int e, int j) { return e * 2 * kTileBytes12 + v_tile * kTileBytes12 + (2 * (wave & 3) + j) * 1024; };
+  auto tile_org = [&](TilePos p) { return (p.kh * W + p.kw) * (kD * 2); };
+  auto v_dma = [&](int e, const sgpr4& rs, TilePos pe) {
+    const TilePos p = v_tile == 0 ? pe : next_tile(pe, H);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int voff, soff;
+      if constexpr (ALIGNED) {
+        voff = v_goff[j];
+        soff = p.kw < W ? tile_org(p) : 0;
+      } else {
+        const int o = 8 * (2 * (wave & 3) + j) + (lane >> 3);
+        const bool ok = p.kh + (o >> 4) < H && p.kw + (o & 15) < W;
+        voff = ok ? tile_org(p) + v_goff[j] : kOob;
+        soff = 0;
+      }
+      const uint32_t dst = static_cast<uint32_t>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) unsigned char*)(raw + raw_off(e, j))));
+      lds_load16(rs, voff, __builtin_amdgcn_readfirstlane(soff),
+                 static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dst))));
+    }
+  };
+  // after this wave's loads are complete: raw -> fp16 (bf16 inputs) -> slot
+  auto v_convert = [&](int e, unsigned char* pair) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(raw + raw_off(e, j) + 16 * lane);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x[w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
+      }
+      *reinterpret_cast<u32x4*>(pair + v_lds[j]) = x;
+    }
+  };
+  // K: wave 8 + kw issues row blocks rb = 4*(kw&1) + i of tile kw>>1 (even,
+  // odd).  Lane L of a row block writes LDS bytes 16L..16L+15 of it: row o =
+  // 8*rb + L/8, swizzled chunk L%8, i.e. logical chunk (L%8) ^ ((o>>1)&7).
+  const int kwv = wave - 8;
+  const int k_tile = kwv >> 1;
+  int k_goff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 8 * (4 * (kwv & 1) + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((o >> 1) & 7);
+    k_goff[i] = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * c;
+  }
+  auto k_dma = [&](const sgpr4& rs, TilePos pe, unsigned char* pair) {
+    const TilePos p = k_tile == 0 ? pe : next_tile(pe, H);
+    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<size_t>(
+        (__attribute__((address_space(3))) unsigned char*)(pair + k_tile * kTileBytes12 + 4 * (kwv & 1) * 1024)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int voff, soff;
+      if constexpr (ALIGNED) {
+        voff = k_goff[i];
+        soff = p.kw < W ? tile_org(p) : 0;
+      } else {
+        const int o = 8 * (4 * (kwv & 1) + i) + (lane >> 3);
+        const bool ok = p.kh + (o >> 4) < H && p.kw + (o & 15) < W;
+        voff = ok ? tile_org(p) + k_goff[i] : kOob;
+        soff = 0;
+      }
+      lds_load16(rs, voff, __builtin_amdgcn_readfirstlane(soff),
+                 static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dst + i * 1024))));
+    }
+  };
+  auto slot_ptr = [&](int s) { return smem + s * kSlotBytes12; };
+
+  // ---- bias ---------------------------------------------------------------------
+  // rel_w through the Q.K^T accumulator (rwc = rel_w * rw_mul per register's
+  // key column, reloaded per 16-column band), rel_h and the reference maximum
+  // in one fma per score (as in the 32-query kernel).
+  const int rows = N - q0 < 32 ? N - q0 : 32;
+  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + (head + q0) * W, static_cast<uint32_t>(rows * W) * 4);
+  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + (head + q0) * H, static_cast<uint32_t>(rows * H) * 4);
+  const int qrow = qok ? ql : 0;
+  const int rw_lane = (qrow * W + 4 * half) * 4;
+  const int rh_lane = qrow * H * 4;
+  f32x16 rwc;
+  auto load_band = [&](int kw0) {
+    float x[8];
+    if constexpr (ALIGNED) {
+      const u32x4 a0 = buf_load16(rwrs, rw_lane, 4 * kw0);
+      const u32x4 a1 = buf_load16(rwrs, rw_lane + 32, 4 * kw0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = as_float(a0[i]) * rw_mul;
+        x[4 + i] = as_float(a1[i]) * rw_mul;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int dc = 8 * (i >> 2) + (i & 3);
+        const int c = kw0 + dc + 4 * half;
+        const float y = buf_loadf(rwrs, c < W ? rw_lane + 4 * (kw0 + dc) : kOob);
+        x[i] = (c < W ? y : -__builtin_inff()) * rw_mul;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rwc[r] = x[4 * ((r >> 2) & 1) + (r & 3)];
+  };
+  float rh[4], rh_next[4];  // rel_h of the step's tile; of the next step's, prefetched
+  auto load_rh = [&](int kh0) {
+    if constexpr (ALIGNED) {
+      const u32x4 a = buf_load16(rhrs, rh_lane, 4 * kh0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rh_next[r] = as_float(a[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float y = buf_loadf(rhrs, kh0 + r < H ? rh_lane + 4 * (kh0 + r) : kOob);
+        rh_next[r] = kh0 + r < H ? y : -__builtin_inff();
+      }
+    }
+  };
+
+  // ---- operand read addressing (bytes within a pair) --------------------------
+  // K^T fragment (st, kd): row 32*st + ql, chunk 2*kd + half, swizzled.
+  int k_rd[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) k_rd[kd] = par * kTileBytes12 + k_off(ql, 2 * kd + half);
+  // V^T fragment (ks, dt): transpose reads of rows 16*ks + tr_row (+8) at 8-byte
+  // unit 8*dt + 4*(grp&1) + (jl&3), units XOR-ed with 8 when bit 1 of the row
+  // (bit 3 of jl) is set.
+  const int grp = lane >> 4, jl = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (jl >> 2);
+  const int vsw = 8 * ((jl >> 3) & 1);
+  int v_rd[2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+    v_rd[dt] = (2 + par) * kTileBytes12 + tr_row * 128 + 8 * ((8 * dt + 4 * (grp & 1) + (jl & 3)) ^ vsw);
+
+  // ---- prologue: pair 0 in slot 0 ---------------------------------------------
+  const TilePos p0{0, 0};
+  if (v_wave) {
+    v_dma(0, vrs0, p0);
+    if (two) v_dma(1, vrs1, p0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    v_convert(0, slot_ptr(0));
+    if (two) v_convert(1, slot_ptr(0) + kPairBytes12);
+  } else {
+    k_dma(krs0, p0, slot_ptr(0));
+    if (two) k_dma(krs1, p0, slot_ptr(0) + kPairBytes12);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  TilePos pc = par ? next_tile(p0, H) : p0;  // this wave's tile of the current step
+  int band_kw = pc.kw;
+  load_band(pc.kw);
+  load_rh(pc.kh);
+  __syncthreads();
+
+  f32x16 acc[2];
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+  float m = 0.f, l = 0.f;
+  bool first = true;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  TilePos pk = next_tile(next_tile(p0, H), H);  // even tile of pair t+1 (staged during step t)
+
+  // This wave's tile of the step, from the pair in `pair` (rel_h already
+  // loaded), as two halves of 32 keys (grid rows 2*st, 2*st+1 of the tile),
+  // each S^T = K Q^T + rel_w term, softmax, O^T += V^T P^T; the first half's
+  // P.V MFMAs are interleaved with the second half's Q.K^T MFMAs (independent
+  // accumulators), so only one half's scores are held at a time.
+  auto compute = [&](const unsigned char* pair) {
+    const unsigned char* kb = pair + hs * kPairBytes12;
+    auto read_k = [&](int st, u32x4 (&kf)[4]) {
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) kf[kd] = *reinterpret_cast<const u32x4*>(kb + k_rd[kd] + st * 32 * 128);
+    };
+    auto read_v = [&](int st, u32x4 (&vf)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const unsigned char* vp = kb + v_rd[dt] + (2 * st + kk) * 16 * 128;
+          const u32x2 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
+          const u32x2 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(vp + 8 * 128));
+          vf[2 * kk + dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    };
+    // Softmax of scores 4g..4g+3 of one half (grid row g/2 of the half):
+    // x = s*c2 + rel_h*log2(e) - m, p = 2^x rounded to fp16 (l sums the
+    // rounded p).
+    auto softmax_chunk = [&](int st, int g, f32x16& sc, u32x4 (&pf)[2], float& tsum) {
+      const float rhm = __builtin_fmaf(rh[2 * st + (g >> 1)], kLog2e, -m);
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = __builtin_fmaf(sc[4 * g + e], c2, rhm);
+        sc[4 * g + e] = x[e];
+      }
+      const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
+      const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum, false);
+      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum, false);
+      pf[g >> 1][2 * (g & 1)] = w0;
+      pf[g >> 1][2 * (g & 1) + 1] = w1;
+    };
+    // After a half's softmax: move the reference maximum when it must (the
+    // first half-tile, or a p above 2^15): the exact maximum of these scores
+    // per query, O and l rescaled, p recomputed.
+    auto settle = [&](f32x16& sc, u32x4 (&pf)[2], float tsum) {
+      const bool grow = first || !(tsum <= kGrowLimit);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        __asm__ volatile("; reference maximum moves" ::);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[r]);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const float inc = first ? mx : __builtin_fmaxf(mx, 0.f);
+        if (!first) {
+          const float alpha = exp2_fast(-inc);
+          l *= alpha;
+          acc[0] *= alpha;
+          acc[1] *= alpha;
+        }
+        m += inc;
+        float ts = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            w4[i] = pack_f16(exp2_fast(sc[8 * gg + 2 * i] - inc), exp2_fast(sc[8 * gg + 2 * i + 1] - inc));
+            ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
+          }
+          pf[gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+        tsum = ts;
+        first = false;
+      }
+      l += tsum;
+    };
+
+    // half 0's Q.K^T; then four chunks of (one Q.K^T MFMA of half 1, the
+    // softmax of four of half 0's scores); then four chunks of (one P.V MFMA
+    // of half 0, the softmax of four of half 1's scores); then half 1's P.V.
+    u32x4 kf[4], vf[4];
+    u32x4 p0[2], p1[2];
+    f32x16 s0, s1;
+    read_k(0, kf);
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) s0 = mfma32<BF16>(kf[kd], qf[kd], kd == 0 ? rwc : s0);
+    // half 1's K fragments are read one chunk ahead of their MFMA
+    auto k1 = [&](int kd) { return *reinterpret_cast<const u32x4*>(kb + k_rd[kd] + 32 * 128); };
+    u32x4 ka = k1(0), kn;
+    __builtin_amdgcn_sched_barrier(0);
+    float ts0 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g < 3) kn = k1(g + 1);
+      s1 = mfma32<BF16>(ka, qf[g], g == 0 ? rwc : s1);
+      softmax_chunk(0, g, s0, p0, ts0);
+      ka = kn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_v(0, vf);
+    settle(s0, p0, ts0);
+    __builtin_amdgcn_sched_barrier(0);
+    float ts1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      acc[g & 1] = mfma32<false>(vf[g], p0[g >> 1], acc[g & 1]);
+      softmax_chunk(1, g, s1, p1, ts1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_v(1, vf);
+    settle(s1, p1, ts1);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[g & 1] = mfma32<false>(vf[g], p1[g >> 1], acc[g & 1]);
+  };
+
+  // One step: the loads of pair t+1 (K straight into the other slot, V into
+  // the raw area) are issued first, then this wave's tile of pair t is
+  // computed from slot t%2; V of pair t+1 is converted into the slot at the
+  // end; barrier.
+  auto step = [&](int t, auto slot_c) {
+    constexpr int cs = decltype(slot_c)::value;  // t % 2
+    unsigned char* nxt = slot_ptr(cs ^ 1);
+    const bool active = 2 * t + par < T;
+    // This step's rel_h (loaded a step ago) and, at a new column band, its
+    // rel_w are waited for before the staging loads are issued: the compiler
+    // does not count those, so a wait it inserted later for an older load
+    // would also wait for them.  Then the next step's rel_h is prefetched.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rh[r] = rh_next[r];
+    __asm__ volatile("" ::"v"(rh[0]), "v"(rh[1]), "v"(rh[2]), "v"(rh[3]));
+    if (active && pc.kw != band_kw) {
+      band_kw = pc.kw;
+      load_band(pc.kw);
+      __asm__ volatile("" ::"v"(rwc[0]), "v"(rwc[4]));
+    }
+    {
+      const TilePos pn = next_tile(next_tile(pc, H), H);
+      if (pn.kw < W) load_rh(pn.kh);
+    }
+    // The loads of pair t+1 (issued right away: their latency is hidden by
+    // this step's compute).
+    auto stage = [&]() {
+      if (v_wave) {
+        v_dma(0, vrs0, pk);
+        if (two) v_dma(1, vrs1, pk);
+      } else {
+        k_dma(krs0, pk, nxt);
+        if (two) k_dma(krs1, pk, nxt + kPairBytes12);
+      }
+    };
+    stage();
+    if (active) compute(slot_ptr(cs));
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (v_wave) {
+      v_convert(0, nxt);
+      if (two) v_convert(1, nxt + kPairBytes12);
+    }
+    __syncthreads();
+    pc = next_tile(next_tile(pc, H), H);
+    pk = next_tile(next_tile(pk, H), H);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < steps; t += 2) {
+    step(t, S0{});
+    step(t + 1, S1{});
+  }
+  if (t < steps) step(t, S0{});
+
+  // ---- merge the two waves of each block through LDS, store ---------------------
+  const float lt = l + __shfl_xor(l, 32);
+  if (first) m = -__builtin_inff();  // a wave with no tile (odd wave, T == 1) carries no weight
+  float* mine = reinterpret_cast<float*>(smem + wave * kMergeStride12);
+  const float* theirs = reinterpret_cast<const float*>(smem + (wave ^ 1) * kMergeStride12);
+  // the partner finalises output columns 32*(1-par) .. : it needs acc[1-par]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[1 - par][r];
+  if (half == 0) {
+    mine[16 * 64 + ql] = m;
+    mine[16 * 64 + 32 + ql] = lt;
+  }
+  __syncthreads();
+  const float mp = theirs[16 * 64 + ql];
+  const float lp = theirs[16 * 64 + 32 + ql];
+  const float mx = __builtin_fmaxf(m, mp);
+  const float wa = exp2_fast(m - mx), wb = exp2_fast(mp - mx);
+  const float inv = 1.0f / (lt * wa + lp * wb);
+  const float ca = wa * inv, cb = wb * inv;
+  if (!bvalid || !qok) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int d = 32 * par + 8 * g + 4 * half;
+    f32x4 o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = acc[par][4 * g + e] * ca + theirs[(4 * g + e) * 64 + lane] * cb;
+    if constexpr (OUT_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
+    } else {
+      const u32x2 pk2 = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
+                             : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (head + qi) * kD + d) = pk2;
+    }
+  }
+}
+
+template <bool BF16, bool OUT_F32, bool ALIGNED>
+hipError_t launch12(const AttnArgs& a, hipStream_t stream) {
+  auto kern = attn12_kernel<BF16, OUT_F32, ALIGNED>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds12);
+  if (err != hipSuccess) return err;
+  const int N = a.H * a.W;
+  const int nblk = (N + 31) / 32;
+  const int total = nblk * a.BH;
+  const int units = (total + kBlocks12 - 1) / kBlocks12;
+  const bool zero_q = a.scale == 0.0f;
+  const float c2 = zero_q ? kLog2e : a.scale * kLog2e;
+  const float rw_mul = zero_q ? 1.0f : kLog2e / c2;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(units)), dim3(kThreads12), kLds12, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out, a.H, a.W, nblk, total, c2,
+                     rw_mul, zero_q ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool OUT_F32>
+hipError_t launch12_al(const AttnArgs& a, hipStream_t stream) {
+  const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
+  return aligned ? launch12<BF16, OUT_F32, true>(a, stream) : launch12<BF16, OUT_F32, false>(a, stream);
+}
+
+}  // namespace
+
+size_t attn12_lds_bytes() { return kLds12; }
+
+bool attn12_fits(int H, int W) {
+  // A workgroup's 6 blocks must span at most two heads.
+  return (H * W + 31) / 32 >= kBlocks12;
+}
+
+hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.out_f32 ? launch12_al<true, true>(a, stream) : launch12_al<true, false>(a, stream);
+  return a.out_f32 ? launch12_al<false, true>(a, stream) : launch12_al<false, false>(a, stream);
+}
+
+}  // namespace relpos

@@ -917,12 +917,14 @@ size_t attn_lds_bytes(int cfg, int H, int W) {
   switch (cfg) {
     case 1: return attn32_lds_bytes<4>();
     case 3: return attn16_lds_bytes();
+    case kAttn12Config: return attn12_lds_bytes();
     default: return attn32_lds_bytes<8>();  // 0 and kAttnSplitConfig
   }
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream) {
   if (cfg == 3) return launch_attn16(a, stream);
+  if (cfg == kAttn12Config) return launch_attn12(a, stream);
   if (a.bf16) {
     return a.out_f32 ? launch_dt<true, true>(a, cfg, stream) : launch_dt<true, false>(a, cfg, stream);
   }

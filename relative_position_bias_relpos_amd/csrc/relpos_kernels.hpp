@@ -52,6 +52,8 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 //   3: 16 queries per wave, 4 waves per workgroup (64 queries)
 //   5: configuration 0 with the key range split over a persistent grid of
 //      split_ctas workgroups (needs the workspace)
+//   6: 12 waves x 32 queries, even and odd key tiles on separate waves
+//      (relpos_attn12.hip)
 constexpr int kAttnSplitConfig = 5;
 // Fixed cost of one segment of the split launch (pipeline start and drain,
 // the piece store, cold K/V tiles at the cut), in key-tile steps, and the
@@ -107,6 +109,14 @@ hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t stream);
 // LDS bytes the attention kernel needs in configuration `cfg`.
 size_t attn_lds_bytes(int cfg, int H, int W);
 hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
+
+// The 12-wave kernel (relpos_attn12.hip): 6 query blocks x even/odd key
+// tiles per workgroup, three waves per SIMD, no workspace.  Needs at least 6
+// query blocks of 32 per head (attn12_fits).
+constexpr int kAttn12Config = 6;
+size_t attn12_lds_bytes();
+bool attn12_fits(int H, int W);
+hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream);
 
 // The 16-query-per-wave kernel (relpos_attn16.hip).
 size_t attn16_lds_bytes();

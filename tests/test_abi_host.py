@@ -128,7 +128,7 @@ def _cfg_call(lib, config, ptrs=None, ws=0, ws_bytes=0, D=64, scale=0.125):
 
 def test_attn_fwd_cfg_argument_checks(lib):
     bad = [x + 2 for x in P]
-    for config in (-1, 0, 1, 3, 5):  # known configurations reach the pointer checks
+    for config in (-1, 0, 1, 3, 5, 6):  # known configurations reach the pointer checks
         assert _cfg_call(lib, config, ptrs=bad) == E_ALIGN, config
     for config in (-2, 2, 4, 7, 1000):
         assert _cfg_call(lib, config, ptrs=bad) == E_VALUE, config

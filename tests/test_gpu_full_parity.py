@@ -5,9 +5,9 @@ bf16), batched fp16 with large logits (4 x 12, 64x64), the rectangular grid
 (2 x 12, 48x80, bf16) and the ViT-L-like grid (2 x 16, 96x96, bf16).  For each,
 the oracle's output is computed once (every head, every row) and compared with
 every output of each launch path: the two-call path as relpos_attn_fwd runs it
-(no workspace), the key-range split (relpos_attn_fwd_cfg, configuration 5) and
-relpos_attn_fused.  Bar: max |gpu - oracle| <= 2e-3 and mean <= 1e-4 over all
-B*heads*N*64 outputs (fp32 out).
+(no workspace), the key-range split (relpos_attn_fwd_cfg, configuration 5), the
+12-wave kernel (configuration 6) and relpos_attn_fused.  Bar: max |gpu - oracle|
+<= 2e-3 and mean <= 1e-4 over all B*heads*N*64 outputs (fp32 out).
 """
 
 import numpy as np
@@ -47,6 +47,12 @@ def test_split_launch(case):
     name, d, ref = case
     out, _, _ = G.gpu_run(d, config=5)
     _check(f"{name} split (configuration 5)", out, ref)
+
+
+def test_twelve_wave_kernel(case):
+    name, d, ref = case
+    out, _, _ = G.gpu_run(d, config=6)
+    _check(f"{name} 12-wave kernel (configuration 6)", out, ref)
 
 
 def test_fused_call(case):

@@ -144,7 +144,7 @@ def test_no_allocation_during_calls():
 
 # ---- every launch configuration ------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [0, 1, 3, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 3, 5, 6])
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("rect", dict(B=1, heads=2, H=21, W=35)),
                                      ("batched_fp16", dict(B=1, heads=2, H=20, W=24))])
 def test_each_launch_config(cfg, name, kw):
