@@ -28,7 +28,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 def kernel_source_hash():
     csrc = os.path.join(ROOT, "relative_position_bias_relpos_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("relpos_attn_fwd.hip", "relpos_attn16.hip", "relpos_attn_common.hpp", "relpos_device.hpp"):
+    for name in ("relpos_attn_fwd.hip", "relpos_attn16.hip", "relpos_attn12.hip", "relpos_attn_common.hpp",
+                 "relpos_device.hpp", "relpos_kernels.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -118,11 +118,16 @@ relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel
  *   in_dtype   RELPOS_BF16 or RELPOS_FP16
  *   out_dtype  RELPOS_FP32, or equal to in_dtype
  *   stream     hipStream_t to enqueue on
- * Value range: P.V runs on fp16 MFMA (P in fp16, fp32 accumulation), so bf16
- * v is converted to fp16 when staged: |v| must stay below 65520 (larger
- * values become inf and the outputs they reach are not finite), and
- * |v| < 2^-24 is flushed to zero (absolute error below 2^-25).  fp16 v is
- * used as is.  Nothing checks the range.
+ * Precision of P.V (fp32 accumulation throughout): for bf16 inputs on grids
+ * of N >= 1024 keys where configuration 6 runs (relpos_attn_config), P is
+ * rounded to bf16 and v used as is; otherwise P is rounded to fp16 and bf16 v
+ * is converted to fp16 when staged.  Rounding P to bf16 adds an error that
+ * averages over the keys (mean |error| 3.5e-5 at 64x64, 2.3e-5 at 96x96 on
+ * N(0,1) inputs, against 4e-6 with fp16 P).
+ * Value range: where bf16 v is converted to fp16, |v| must stay below 65520
+ * (larger values become inf and the outputs they reach are not finite), and
+ * |v| < 2^-24 is flushed to zero (absolute error below 2^-25).  fp16 v, and
+ * bf16 v with bf16 P, are used as is.  Nothing checks the range.
  * Errors: E_SHAPE, E_DTYPE, E_VALUE, E_NULL, E_ALIGN, E_DEVICE, E_ALIAS, E_LAUNCH.
  */
 relpos_status relpos_attn_fwd(const void* q, const void* k, const void* v,
@@ -245,6 +250,13 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  *      ceil(W/16) <= 4), where its shorter pipeline is measured fastest.
  *   5: configuration 0 with the key range split over one workgroup per
  *      compute unit (relpos_attn_fwd_ws only).
+ *   6: workgroups of 12 waves over 6 blocks of 32 queries, one workgroup per
+ *      compute unit; the two waves of a block take the even and the odd key
+ *      tiles and merge at the end, and a workgroup may cover the last blocks
+ *      of one (b, h) and the first of the next.  Needs N >= 192 and the full
+ *      160 KB LDS.  Considered for bf16 inputs with N >= 1024 (where its P.V
+ *      runs in bf16), at 0.75 * 1.05 of a configuration-0 round per round of
+ *      ceil(B*heads*ceil(N/32)/6) workgroups.
  *
  * Otherwise the choice compares times in workgroup rounds (one round = one 4-wave
  * workgroup per SIMD pair of every compute unit running all T key tiles of

@@ -155,6 +155,22 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
   const int64_t full = g4 / (2 * cus), rem = g4 % (2 * cus);
   const double t4 = static_cast<double>(full) + (rem == 0 ? 0.0 : (rem <= cus ? 0.77 : 1.0));
   int best = t8 <= t4 ? 0 : 1;
+  double tbest = best == 0 ? t8 : t4;
+  // 12-wave kernel (configuration 6), bf16 inputs on grids where it runs
+  // P.V in bf16 and so stages V without conversion: one workgroup of 192
+  // queries per CU, a round taken as 0.75 * 1.05 of an 8-wave round.  The
+  // finer grain fills CUs that 256-query units leave idle.  Measured (us,
+  // configuration 6 / 0 / split): 64x64 x 12 heads 67.8 / 73.8 / 75.4, 48x80
+  // x 24 heads 116.7 / 142.0 / 124.8, 96x96 x 32 heads 802 / 893 / 841.
+  if (bf16 && relpos::attn12_bf16_p(static_cast<int>(H), static_cast<int>(W)) &&
+      relpos::attn12_fits(static_cast<int>(H), static_cast<int>(W))) {
+    const int64_t g12 = (BH * ((N + 31) / 32) + 5) / 6;
+    const double t12 = a8 * 0.75 * 1.05 * static_cast<double>((g12 + cus - 1) / cus);
+    if (t12 < tbest) {
+      best = relpos::kAttn12Config;
+      tbest = t12;
+    }
+  }
   // Split: the full rounds of 8-wave units, then a last round whose heads
   // and tails (k per idle CU) take max(s + F, k*(T - s + F)) tiles with F =
   // kSplitSegmentTiles per segment, plus the merge, all at kSplitGridFactor
@@ -168,7 +184,7 @@ int attn_auto_config(int64_t BH, int64_t H, int64_t W, bool bf16, int cus, bool 
       const int64_t last = head > tails ? head : tails;
       const double ts = a8 * relpos::kSplitGridFactor *
                         (sp.rounds + static_cast<double>(last + relpos::kMergeTiles) / static_cast<double>(T));
-      if (ts < (best == 0 ? t8 : t4)) best = relpos::kAttnSplitConfig;
+      if (ts < tbest) best = relpos::kAttnSplitConfig;
     }
   }
   return best;

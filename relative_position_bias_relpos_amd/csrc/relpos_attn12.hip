@@ -15,12 +15,15 @@
 //     and merge through LDS at the end; each writes half of the block's
 //     output columns.  No workspace.
 //   * Per step the workgroup stages one tile pair (the next even and odd tile)
-//     per head it spans: K by LDS-direct 16-byte buffer loads (no registers),
-//     V through registers (bf16 is converted to fp16 on the way, so that P.V
-//     runs on fp16 MFMA with fp16 P).  Two LDS slots (step t reads slot t%2
-//     while step t+1's pair is written to the other); V's global loads run one
-//     step ahead.  Tiles are unpadded (8 KB) with XOR-swizzled 16-byte chunks
-//     so the MFMA operand reads hit every LDS bank once.
+//     per head it spans, all by LDS-direct 16-byte buffer loads that pass no
+//     data through registers: 8 waves load V, 4 load K, at the top of step t
+//     into the slot step t+1 reads (two LDS slots).  P.V runs on bf16 MFMA
+//     with P rounded to bf16 for bf16 inputs on grids of >= 1024 keys, so V is
+//     staged as loaded; fp16 inputs likewise in fp16.  Otherwise (bf16, fewer
+//     keys) P is fp16, and bf16 V lands in a raw area first and each V wave
+//     converts its own 16 bytes per lane to fp16 at the end of the step.
+//     Tiles are unpadded (8 KB) with XOR-swizzled 16-byte chunks so the MFMA
+//     operand reads hit every LDS bank once.
 //   * Inside a wave a step is plain: S^T = K Q^T (32x32x16 MFMA, rel_w in the
 //     accumulator's initial value), exp2 softmax with a lazy reference maximum,
 //     O^T += V^T P^T.  The three waves of a SIMD overlap one another's MFMA
@@ -48,6 +51,13 @@ constexpr int kSlotBytes12 = 2 * kPairBytes12;     // one pair per head spanned
 constexpr int kRawBytes12 = 2 * 2 * kTileBytes12;   // V of a pair as loaded, per head (before conversion)
 constexpr int kLds12 = 2 * kSlotBytes12 + kRawBytes12;  // two slots + the raw V area: 160 KB
 constexpr int kMergeStride12 = 64 * 16 * 4 + 2 * 32 * 4;  // per wave: 16 accumulators per lane, m, l
+// bf16 inputs with at least this many keys run P.V in bf16.  Rounding p to
+// bf16 (8 significant bits) adds to each output an error that averages out
+// over the keys; emulated in float64 on the workloads here, its mean over
+// the outputs is 3.4e-5 at N = 4096 and 2.3e-5 at N = 9216 (1.2e-4 at N =
+// 256), against a 1e-4 bar, and it falls as 1/sqrt(N).  Smaller grids keep
+// fp16 P.
+constexpr int kBf16PMinKeys = 1024;
 
 // Byte offset of K chunk c (16 bytes, d = 8c .. 8c+7) of tile row o: rows of
 // 128 bytes, chunk index XOR-ed with bits 1..3 of the row, so that the 16
@@ -87,7 +97,9 @@ __device__ __forceinline__ void lds_load16(sgpr4 rs, int voff, int soff, uint32_
       : "memory", "m0");
 }
 
-template <bool BF16, bool OUT_F32, bool ALIGNED>
+// PB (bf16 inputs only): P.V runs in bf16 (P rounded to bf16, V staged as
+// loaded); otherwise in fp16 (bf16 V converted to fp16 while staged).
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB>
 __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
@@ -155,30 +167,40 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     v_lds[j] = (2 + v_tile) * kTileBytes12 + v_off(o, lane & 7);
   }
   unsigned char* raw = smem + 2 * kSlotBytes12;
+  // LDS byte address of smem (wave-uniform): the LDS-direct loads take their
+  // destination as a scalar
+  const uint32_t lds0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) unsigned char*)smem))));
   auto raw_off = [&](int e, int j) { return e * 2 * kTileBytes12 + v_tile * kTileBytes12 + (2 * (wave & 3) + j) * 1024; };
   auto tile_org = [&](TilePos p) { return (p.kh * W + p.kw) * (kD * 2); };
-  auto v_dma = [&](int e, const sgpr4& rs, TilePos pe) {
+  // V to convert (bf16 inputs with fp16 P): into the raw area, converted
+  // later; otherwise straight into the slot's swizzled V tile (lane L then
+  // loads logical chunk (L%8) ^ (4*bit 1 of the row), as K does).
+  // pair_off: the pair's LDS offset.
+  constexpr bool kConvertV = BF16 && !PB;
+  auto v_dma = [&](int e, const sgpr4& rs, TilePos pe, int pair_off) {
     const TilePos p = v_tile == 0 ? pe : next_tile(pe, H);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      const int o = 8 * (2 * (wave & 3) + j) + (lane >> 3);
+      const int gchunk = kConvertV ? 0 : 16 * (((lane & 7) ^ (4 * ((o >> 1) & 1))) - (lane & 7));
       int voff, soff;
       if constexpr (ALIGNED) {
-        voff = v_goff[j];
+        voff = v_goff[j] + gchunk;
         soff = p.kw < W ? tile_org(p) : 0;
       } else {
-        const int o = 8 * (2 * (wave & 3) + j) + (lane >> 3);
         const bool ok = p.kh + (o >> 4) < H && p.kw + (o & 15) < W;
-        voff = ok ? tile_org(p) + v_goff[j] : kOob;
+        voff = ok ? tile_org(p) + v_goff[j] + gchunk : kOob;
         soff = 0;
       }
-      const uint32_t dst = static_cast<uint32_t>(
-          reinterpret_cast<size_t>((__attribute__((address_space(3))) unsigned char*)(raw + raw_off(e, j))));
-      lds_load16(rs, voff, __builtin_amdgcn_readfirstlane(soff),
-                 static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dst))));
+      const uint32_t dst = kConvertV ? lds0 + 2 * kSlotBytes12 + raw_off(e, j)
+                                     : lds0 + pair_off + (2 + v_tile) * kTileBytes12 + (2 * (wave & 3) + j) * 1024;
+      lds_load16(rs, voff, soff, dst);
     }
   };
-  // after this wave's loads are complete: raw -> fp16 (bf16 inputs) -> slot
+  // bf16 V for fp16 P, after this wave's loads are complete: raw -> fp16 -> slot
   auto v_convert = [&](int e, unsigned char* pair) {
+    if constexpr (!kConvertV) return;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       u32x4 x = *reinterpret_cast<const u32x4*>(raw + raw_off(e, j) + 16 * lane);
@@ -201,10 +223,10 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     const int c = (lane & 7) ^ ((o >> 1) & 7);
     k_goff[i] = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * c;
   }
-  auto k_dma = [&](const sgpr4& rs, TilePos pe, unsigned char* pair) {
+  // pair_off: byte offset of the pair in LDS
+  auto k_dma = [&](const sgpr4& rs, TilePos pe, int pair_off) {
     const TilePos p = k_tile == 0 ? pe : next_tile(pe, H);
-    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<size_t>(
-        (__attribute__((address_space(3))) unsigned char*)(pair + k_tile * kTileBytes12 + 4 * (kwv & 1) * 1024)));
+    const uint32_t dst = lds0 + pair_off + k_tile * kTileBytes12 + 4 * (kwv & 1) * 1024;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int voff, soff;
@@ -217,8 +239,7 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
         voff = ok ? tile_org(p) + k_goff[i] : kOob;
         soff = 0;
       }
-      lds_load16(rs, voff, __builtin_amdgcn_readfirstlane(soff),
-                 static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dst + i * 1024))));
+      lds_load16(rs, voff, soff, dst + i * 1024);
     }
   };
   auto slot_ptr = [&](int s) { return smem + s * kSlotBytes12; };
@@ -290,14 +311,14 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   // ---- prologue: pair 0 in slot 0 ---------------------------------------------
   const TilePos p0{0, 0};
   if (v_wave) {
-    v_dma(0, vrs0, p0);
-    if (two) v_dma(1, vrs1, p0);
+    v_dma(0, vrs0, p0, 0);
+    if (two) v_dma(1, vrs1, p0, kPairBytes12);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     v_convert(0, slot_ptr(0));
     if (two) v_convert(1, slot_ptr(0) + kPairBytes12);
   } else {
-    k_dma(krs0, p0, slot_ptr(0));
-    if (two) k_dma(krs1, p0, slot_ptr(0) + kPairBytes12);
+    k_dma(krs0, p0, 0);
+    if (two) k_dma(krs1, p0, kPairBytes12);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   TilePos pc = par ? next_tile(p0, H) : p0;  // this wave's tile of the current step
@@ -311,7 +332,23 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   acc[1] = f32x16{};
   float m = 0.f, l = 0.f;
   bool first = true;
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // p packing and the row sum of the rounded p, in P's type
+  auto pack_p = [](float a, float b) -> uint32_t {
+    if constexpr (PB) {
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+    } else {
+      return pack_f16(a, b);
+    }
+  };
+  auto sum_p = [](uint32_t w, float acc_) -> float {
+    if constexpr (PB) {
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), bf16x2{(__bf16)1.0f, (__bf16)1.0f},
+                                             acc_, false);
+    } else {
+      return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc_,
+                                    false);
+    }
+  };
 
   TilePos pk = next_tile(next_tile(p0, H), H);  // even tile of pair t+1 (staged during step t)
 
@@ -320,7 +357,7 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   // each S^T = K Q^T + rel_w term, softmax, O^T += V^T P^T; the first half's
   // P.V MFMAs are interleaved with the second half's Q.K^T MFMAs (independent
   // accumulators), so only one half's scores are held at a time.
-  auto compute = [&](const unsigned char* pair) {
+  auto compute = [&](const unsigned char* pair, auto&& tail) {
     const unsigned char* kb = pair + hs * kPairBytes12;
     auto read_k = [&](int st, u32x4 (&kf)[4]) {
 #pragma unroll
@@ -349,10 +386,10 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
         x[e] = __builtin_fmaf(sc[4 * g + e], c2, rhm);
         sc[4 * g + e] = x[e];
       }
-      const uint32_t w0 = pack_f16(exp2_fast(x[0]), exp2_fast(x[1]));
-      const uint32_t w1 = pack_f16(exp2_fast(x[2]), exp2_fast(x[3]));
-      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), ones, tsum, false);
-      tsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), ones, tsum, false);
+      const uint32_t w0 = pack_p(exp2_fast(x[0]), exp2_fast(x[1]));
+      const uint32_t w1 = pack_p(exp2_fast(x[2]), exp2_fast(x[3]));
+      tsum = sum_p(w0, tsum);
+      tsum = sum_p(w1, tsum);
       pf[g >> 1][2 * (g & 1)] = w0;
       pf[g >> 1][2 * (g & 1) + 1] = w1;
     };
@@ -367,8 +404,10 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[r]);
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const float inc = first ? mx : __builtin_fmaxf(mx, 0.f);
-        if (!first) {
+        // an idle step's scores are all -inf: no maximum to take, p = 0
+        const bool empty = !(mx > -__builtin_inff());
+        const float inc = empty ? 0.f : (first ? mx : __builtin_fmaxf(mx, 0.f));
+        if (!first && !empty) {
           const float alpha = exp2_fast(-inc);
           l *= alpha;
           acc[0] *= alpha;
@@ -381,13 +420,13 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
           uint32_t w4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            w4[i] = pack_f16(exp2_fast(sc[8 * gg + 2 * i] - inc), exp2_fast(sc[8 * gg + 2 * i + 1] - inc));
-            ts = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[i]), ones, ts, false);
+            w4[i] = pack_p(exp2_fast(sc[8 * gg + 2 * i] - inc), exp2_fast(sc[8 * gg + 2 * i + 1] - inc));
+            ts = sum_p(w4[i], ts);
           }
           pf[gg] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
         tsum = ts;
-        first = false;
+        if (!empty) first = false;
       }
       l += tsum;
     };
@@ -420,20 +459,23 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     float ts1 = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      acc[g & 1] = mfma32<false>(vf[g], p0[g >> 1], acc[g & 1]);
+      acc[g & 1] = mfma32<PB>(vf[g], p0[g >> 1], acc[g & 1]);
       softmax_chunk(1, g, s1, p1, ts1);
       __builtin_amdgcn_sched_barrier(0);
     }
     read_v(1, vf);
     settle(s1, p1, ts1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the step's staging tail (V conversion) runs beside the last P.V MFMAs
+    tail();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) acc[g & 1] = mfma32<false>(vf[g], p1[g >> 1], acc[g & 1]);
+    for (int g = 0; g < 4; ++g) acc[g & 1] = mfma32<PB>(vf[g], p1[g >> 1], acc[g & 1]);
   };
 
   // One step: the loads of pair t+1 (K straight into the other slot, V into
   // the raw area) are issued first, then this wave's tile of pair t is
-  // computed from slot t%2; V of pair t+1 is converted into the slot at the
-  // end; barrier.
+  // computed from slot t%2; V of pair t+1 is converted into the other slot
+  // beside the tile's last MFMAs; barrier.
   auto step = [&](int t, auto slot_c) {
     constexpr int cs = decltype(slot_c)::value;  // t % 2
     unsigned char* nxt = slot_ptr(cs ^ 1);
@@ -442,8 +484,11 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     // rel_w are waited for before the staging loads are issued: the compiler
     // does not count those, so a wait it inserted later for an older load
     // would also wait for them.  Then the next step's rel_h is prefetched.
+    // An idle step (the odd wave's last one when T is odd) runs the same code
+    // with rel_h = -inf: every score is -inf, every p 0, and O, l, m stay as
+    // they are (a branch around the tile would make the compiler copy O).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rh[r] = rh_next[r];
+    for (int r = 0; r < 4; ++r) rh[r] = active ? rh_next[r] : -__builtin_inff();
     __asm__ volatile("" ::"v"(rh[0]), "v"(rh[1]), "v"(rh[2]), "v"(rh[3]));
     if (active && pc.kw != band_kw) {
       band_kw = pc.kw;
@@ -458,20 +503,21 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     // this step's compute).
     auto stage = [&]() {
       if (v_wave) {
-        v_dma(0, vrs0, pk);
-        if (two) v_dma(1, vrs1, pk);
+        v_dma(0, vrs0, pk, (cs ^ 1) * kSlotBytes12);
+        if (two) v_dma(1, vrs1, pk, (cs ^ 1) * kSlotBytes12 + kPairBytes12);
       } else {
-        k_dma(krs0, pk, nxt);
-        if (two) k_dma(krs1, pk, nxt + kPairBytes12);
+        k_dma(krs0, pk, (cs ^ 1) * kSlotBytes12);
+        if (two) k_dma(krs1, pk, (cs ^ 1) * kSlotBytes12 + kPairBytes12);
       }
     };
     stage();
-    if (active) compute(slot_ptr(cs));
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (v_wave) {
-      v_convert(0, nxt);
-      if (two) v_convert(1, nxt + kPairBytes12);
-    }
+    compute(slot_ptr(cs), [&]() {
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (v_wave) {
+        v_convert(0, nxt);
+        if (two) v_convert(1, nxt + kPairBytes12);
+      }
+    });
     __syncthreads();
     pc = next_tile(next_tile(pc, H), H);
     pk = next_tile(next_tile(pk, H), H);
@@ -488,7 +534,7 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
 
   // ---- merge the two waves of each block through LDS, store ---------------------
   const float lt = l + __shfl_xor(l, 32);
-  if (first) m = -__builtin_inff();  // a wave with no tile (odd wave, T == 1) carries no weight
+  if (lt == 0.0f) m = -__builtin_inff();  // a wave with no key (odd wave, T == 1) carries no weight
   float* mine = reinterpret_cast<float*>(smem + wave * kMergeStride12);
   const float* theirs = reinterpret_cast<const float*>(smem + (wave ^ 1) * kMergeStride12);
   // the partner finalises output columns 32*(1-par) .. : it needs acc[1-par]
@@ -522,9 +568,9 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32, bool ALIGNED>
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB>
 hipError_t launch12(const AttnArgs& a, hipStream_t stream) {
-  auto kern = attn12_kernel<BF16, OUT_F32, ALIGNED>;
+  auto kern = attn12_kernel<BF16, OUT_F32, ALIGNED, PB>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds12);
   if (err != hipSuccess) return err;
@@ -542,15 +588,17 @@ hipError_t launch12(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool OUT_F32>
+template <bool BF16, bool OUT_F32, bool PB>
 hipError_t launch12_al(const AttnArgs& a, hipStream_t stream) {
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch12<BF16, OUT_F32, true>(a, stream) : launch12<BF16, OUT_F32, false>(a, stream);
+  return aligned ? launch12<BF16, OUT_F32, true, PB>(a, stream) : launch12<BF16, OUT_F32, false, PB>(a, stream);
 }
 
 }  // namespace
 
 size_t attn12_lds_bytes() { return kLds12; }
+
+bool attn12_bf16_p(int H, int W) { return H * W >= kBf16PMinKeys; }
 
 bool attn12_fits(int H, int W) {
   // A workgroup's 6 blocks must span at most two heads.
@@ -558,8 +606,12 @@ bool attn12_fits(int H, int W) {
 }
 
 hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.out_f32 ? launch12_al<true, true>(a, stream) : launch12_al<true, false>(a, stream);
-  return a.out_f32 ? launch12_al<false, true>(a, stream) : launch12_al<false, false>(a, stream);
+  if (a.bf16) {
+    if (attn12_bf16_p(a.H, a.W))
+      return a.out_f32 ? launch12_al<true, true, true>(a, stream) : launch12_al<true, false, true>(a, stream);
+    return a.out_f32 ? launch12_al<true, true, false>(a, stream) : launch12_al<true, false, false>(a, stream);
+  }
+  return a.out_f32 ? launch12_al<false, true, false>(a, stream) : launch12_al<false, false, false>(a, stream);
 }
 
 }  // namespace relpos

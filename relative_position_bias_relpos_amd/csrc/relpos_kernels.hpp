@@ -116,6 +116,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int cfg, hipStream_t stream);
 constexpr int kAttn12Config = 6;
 size_t attn12_lds_bytes();
 bool attn12_fits(int H, int W);
+// Whether the kernel runs P.V in bf16 for bf16 inputs on this grid.
+bool attn12_bf16_p(int H, int W);
 hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream);
 
 // The 16-query-per-wave kernel (relpos_attn16.hip).

@@ -189,19 +189,41 @@ def _ws_bytes(lib, B, heads, H, W, dt, cus=256):
     return lib.relpos_attn_workspace_bytes(B, heads, H, W, dt, cus)
 
 
+TWELVE = 6
+
+
 def test_attn_config_on_the_workloads(lib):
-    # 64x64, 12 heads: 192 workgroups of 8 waves fit in one round; 384 of 4
-    # waves leave half the CUs with two workgroups -> 8 waves.
-    assert _cfg(lib, 1, 12, 64, 64, BF16) == 0
-    # 48x80, 2x12 heads: 360 workgroups of 8 waves need two full rounds; 720
-    # of 4 waves end with 208 lone workgroups -> 4 waves.
-    assert _cfg(lib, 2, 12, 48, 80, BF16) == 1
-    # 96x96, 2x16 heads: 5 rounds x 0.91 = 4.55 against 4 + 0.77.
-    assert _cfg(lib, 2, 16, 96, 96, BF16) == 0
-    # fp16 64x64, 4x12 heads: 3 rounds each; without a V conversion to share,
-    # an 8-wave round counts 0.985 -> 8 waves, by a small margin.
-    assert _cfg(lib, 4, 12, 64, 64, FP16) == 0
+    # bf16 with N >= 1024: the 12-wave kernel (192 queries per workgroup, a
+    # round at 0.91 * 0.75 * 1.05 = 0.717).
+    # 64x64, 12 heads: 1536 blocks of 32 = 256 workgroups, one round (0.717),
+    # against 192 8-wave workgroups in one round (0.91).
+    assert _cfg(lib, 1, 12, 64, 64, BF16) == TWELVE
+    # 48x80, 2x12 heads: 480 workgroups, two rounds (1.43), against 8 waves
+    # (360 workgroups, two rounds: 1.82) and 4 waves (720: 1 + 0.77).
+    assert _cfg(lib, 2, 12, 48, 80, BF16) == TWELVE
+    # 96x96, 2x16 heads: 1536 workgroups, six rounds (4.30), against 5 rounds
+    # x 0.91 = 4.55 and 4 + 0.77.
+    assert _cfg(lib, 2, 16, 96, 96, BF16) == TWELVE
+    # bf16 64x64, 4x12 heads: four 12-wave rounds (2.87) against three 8-wave
+    # rounds (2.73).
     assert _cfg(lib, 4, 12, 64, 64, BF16) == 0
+    # fp16 64x64, 4x12 heads: 3 rounds each; without a V conversion to share,
+    # an 8-wave round counts 0.985 -> 8 waves, by a small margin.  fp16 never
+    # takes the 12-wave kernel.
+    assert _cfg(lib, 4, 12, 64, 64, FP16) == 0
+    assert _cfg(lib, 2, 16, 96, 96, FP16) == 1
+
+
+def test_attn_config_twelve_wave_limits(lib):
+    # bf16 below 1024 keys (fp16 P there) is left to the other kernels:
+    # 16x32 grids, 96 heads = 3072 blocks of 32 would be 512 workgroups.
+    assert _cfg(lib, 1, 96, 16, 32, BF16) != TWELVE
+    # From 1024 keys on: 16x64, 12 heads, 64 workgroups in one round.
+    assert _cfg(lib, 1, 12, 16, 64, BF16) == TWELVE
+    # More than one round where 8-wave units fill the chip evenly: 64x64 with
+    # 16 heads is exactly 256 8-wave workgroups (0.91) against 342 12-wave
+    # workgroups (two rounds, 1.43).
+    assert _cfg(lib, 1, 16, 64, 64, BF16) == 0
 
 
 def test_attn_config_rounds_arithmetic(lib):
@@ -219,8 +241,11 @@ def test_attn_config_rounds_arithmetic(lib):
     # half empty (four rounds) against two full 4-wave rounds.
     assert _cfg(lib, 1, 1024, 32, 4, BF16) == 1
     # The CU count enters: on 128 CUs the 64x64 workload needs two 8-wave
-    # rounds (1.82) against 384 = 1.5 rounds of 4 waves (1 + 0.77).
-    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128) == 1
+    # rounds (1.82) against 384 = 1.5 rounds of 4 waves (1 + 0.77); fp16,
+    # for which the 12-wave kernel is not considered, takes 4 waves.
+    assert _cfg(lib, 1, 12, 64, 64, FP16, cus=128) == 1
+    # bf16: 256 12-wave workgroups on 128 CUs, two rounds (1.43).
+    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128) == 6
 
 
 def test_attn_config_short_key_loops(lib):
@@ -245,31 +270,42 @@ def test_attn_config_with_workspace(lib):
     # 64x64, 12 heads: 192 units of 64 tiles on 256 CUs, no full round; the
     # 64 idle CUs take 3 tails each.  With 6 tiles per segment, s = (3*64 +
     # 2*6) / 4 = 51: head 51 + 6 = 57, tails 3 * (13 + 6) = 57, so
-    # 0.91 * 1.06 * (57 + 4) / 64 = 0.919 rounds against 0.91 unsplit -> no split.
-    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == 0
+    # 0.91 * 1.06 * (57 + 4) / 64 = 0.919 rounds against 0.91 unsplit and
+    # 0.717 for the 12-wave kernel.
+    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=1) == TWELVE
+    assert _cfg(lib, 1, 12, 64, 64, FP16, ws=1) == 0
     # 48x80, 2x12 heads: 360 units of 60 tiles: one full round, then 104 units
-    # cut at s = 30 (k = 1): 0.91 * 1.06 * (1 + (36 + 4) / 60) = 1.61 against 1.77.
-    assert _cfg(lib, 2, 12, 48, 80, BF16, ws=1) == SPLIT
+    # cut at s = 30 (k = 1): 0.91 * 1.06 * (1 + (36 + 4) / 60) = 1.61 against
+    # 1.77 unsplit, but 1.43 for the 12-wave kernel; fp16 splits.
+    assert _cfg(lib, 2, 12, 48, 80, BF16, ws=1) == TWELVE
+    assert _cfg(lib, 2, 12, 48, 80, FP16, ws=1) == SPLIT
     # 96x96, 2x16 heads: 1152 units of 144 tiles: 4 rounds, then 128 cut at
-    # s = 72: 0.91 * 1.06 * (4 + (78 + 4) / 144) = 4.41 < 4.55.
-    assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == SPLIT
+    # s = 72: 0.91 * 1.06 * (4 + (78 + 4) / 144) = 4.41 < 4.55, but 4.30 for
+    # the 12-wave kernel.  fp16 with 16 heads: 2 rounds + 64 units cut,
+    # 0.985 * 1.06 * (2 + 82 / 144) = 2.68 against 2 + 0.77.
+    assert _cfg(lib, 2, 16, 96, 96, BF16, ws=1) == TWELVE
+    assert _cfg(lib, 1, 16, 96, 96, FP16, ws=1) == SPLIT
     # fp16 64x64, 4x12 heads: 768 units = 3 whole rounds; splitting gains nothing.
     assert _cfg(lib, 4, 12, 64, 64, FP16, ws=1) == 0
     # 16x16, 2 heads: 4 key tiles per unit -> the 16-query kernel, split or not.
     assert _cfg(lib, 1, 2, 16, 16, BF16, ws=1) == 3
     # without a workspace the split is never chosen
-    assert _cfg(lib, 1, 12, 64, 64, BF16, ws=0) == 0
+    assert _cfg(lib, 1, 16, 96, 96, FP16, ws=0) == 1
 
 
 def test_workspace_bytes(lib):
     # two piece slots of (256*64 + 2*256) floats per compute unit
-    assert _ws_bytes(lib, 2, 16, 96, 96, BF16) == 256 * 2 * (256 * 64 + 512) * 4
-    # 64x64, 12 heads on 256 CUs: the unsplit launch is chosen -> no workspace
+    assert _ws_bytes(lib, 1, 16, 96, 96, FP16) == 256 * 2 * (256 * 64 + 512) * 4
+    # 64x64, 12 heads on 256 CUs: the 12-wave kernel is chosen -> no workspace
     assert _ws_bytes(lib, 1, 12, 64, 64, BF16) == 0
-    # 64x64, 12 heads on 128 CUs: one full round of 128 units, then 64 units
-    # split at tile 32: 0.91 * 1.06 * (1 + (38 + 4) / 64) = 1.60 against 1.77.
-    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128, ws=1) == 5
-    assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=128) == 128 * 2 * (256 * 64 + 512) * 4
+    assert _ws_bytes(lib, 2, 16, 96, 96, BF16) == 0
+    # 64x64, 12 fp16 heads on 128 CUs: one full round of 128 units, then 64
+    # units split at tile 32: 0.985 * 1.06 * (1 + (38 + 4) / 64) = 1.73
+    # against 1.77.  (bf16: two 12-wave rounds, 1.43.)
+    assert _cfg(lib, 1, 12, 64, 64, FP16, cus=128, ws=1) == 5
+    assert _ws_bytes(lib, 1, 12, 64, 64, FP16, cus=128) == 128 * 2 * (256 * 64 + 512) * 4
+    assert _cfg(lib, 1, 12, 64, 64, BF16, cus=128, ws=1) == 6
+    assert _ws_bytes(lib, 1, 12, 64, 64, BF16, cus=128) == 0
     # 16x32 grid, 150 heads, 128 CUs: 300 units of 8 tiles, 2 rounds + 44
     # split at tile 4: 0.91 * 1.06 * (2 + (10 + 4) / 8) = 3.62; three 8-wave
     # rounds (2.73) beat 2 + 0.77 4-wave rounds.

@@ -195,10 +195,10 @@ def test_forced_split_full(name, kw):
 
 
 def test_split_chosen_with_a_workspace():
-    """relpos_attn_fwd_ws with a workspace splits the 96x96 workload (the cost
-    model's choice there) and asks for the documented workspace size."""
+    """relpos_attn_fwd_ws with a workspace splits 16 fp16 heads of 96x96 (the
+    cost model's choice there) and asks for the documented workspace size."""
     from relative_position_bias_relpos_amd import binding as rp
-    d = G.make("vitl")
+    d = G.make("vitl", B=1, dtype="fp16")
     B, nh = d["q"].shape[:2]
     assert rp.attn_config(B, nh, d["H"], d["W"], d["q"].dtype, G.cu_count(), with_workspace=True) == 5
     assert rp.workspace_bytes(B, nh, d["H"], d["W"], d["q"].dtype, G.cu_count()) == G.split_ws_bytes()
@@ -209,7 +209,7 @@ def test_split_chosen_with_a_workspace():
 
 def test_split_workspace_errors():
     from relative_position_bias_relpos_amd import binding as rp
-    d = G.make("vitl", B=1)  # 16 heads of 96x96: the cost model splits it
+    d = G.make("vitl", B=1, dtype="fp16")  # 16 fp16 heads of 96x96: the cost model splits it
     g = G.to_dev(d)
     rel_h, rel_w = rp.relpos_build(g["q"], g["rel_pos_h"], g["rel_pos_w"], d["H"], d["W"])
     small = torch.zeros(1024, dtype=torch.uint8, device="cuda")
