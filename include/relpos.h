@@ -21,8 +21,11 @@
  * Conventions shared by every call:
  *   - All tensors are dense, row-major, 16-byte aligned, and live in device
  *     memory of the current HIP device (hipSetDevice).  The caller allocates and
- *     owns every buffer; the library allocates nothing, keeps no state besides a
- *     per-device cache of device properties, and never synchronises the host.
+ *     owns every buffer; the library allocates nothing at run time, keeps no
+ *     state besides a per-device cache of device properties and the fixed
+ *     scratch array of relpos_attn_fused_noalloc (RELPOS_SCRATCH_BYTES per
+ *     device, reserved when the library's device code is loaded), and never
+ *     synchronises the host.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL means the null stream)
  *     and completes asynchronously.  Calls are safe from several host threads.
  *   - Checks run in this order, and the first failure is returned: sizes
@@ -225,6 +228,36 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
                                 int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
                                 float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
                                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Size of the per-device scratch array behind relpos_attn_fused_noalloc. */
+#define RELPOS_SCRATCH_BYTES (96u << 20)
+
+/*
+ * relpos_attn_fused_noalloc: relpos_attn_fused for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * serving loops that forbid allocation).  The workspace is a fixed array of
+ * RELPOS_SCRATCH_BYTES (96 MiB) of device memory per device, held by the
+ * library from the load of its device code to the end of the process; the
+ * call itself allocates nothing.
+ *
+ * Same operation, arguments (without workspace and workspace_bytes), result
+ * and errors as relpos_attn_fused, plus
+ *   E_SHAPE  when relpos_fused_workspace_bytes(...) for the current device
+ *            exceeds RELPOS_SCRATCH_BYTES (on 256 compute units: when
+ *            roundup(H, 4) + roundup(W, 16) > 252; 64x64, 48x80 and 96x96
+ *            fit).
+ *   E_HIP    when the scratch array's address cannot be looked up.
+ * The scratch contents are never read before they are written within a call,
+ * so nothing needs clearing between calls.  Every call on one device shares
+ * that device's array: calls on one stream are ordered, but calls that can
+ * overlap on one device (several streams, several host threads) race and must
+ * not be issued.
+ */
+relpos_status relpos_attn_fused_noalloc(const void* q, const void* k, const void* v,
+                                        const void* rel_pos_h, const void* rel_pos_w, void* out,
+                                        int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                        float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                        void* stream);
 
 /*
  * relpos_fused_workspace_bytes: workspace bytes relpos_attn_fused needs on a

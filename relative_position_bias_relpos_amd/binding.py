@@ -58,6 +58,9 @@ def _load():
         lib.relpos_attn_fused.restype = i32
         lib.relpos_attn_fused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32,
                                           vp, i64, vp]
+        lib.relpos_attn_fused_noalloc.restype = i32
+        lib.relpos_attn_fused_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32,
+                                                  vp]
         lib.relpos_fused_workspace_bytes.restype = i64
         lib.relpos_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         lib.relpos_attn_config.restype = i32
@@ -244,16 +247,7 @@ def relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=None, out_dtype=torc
     return out
 
 
-def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_dtype=torch.float32,
-                      workspace="auto"):
-    """relpos_build and relpos_attn_fwd in one launch: out [B,heads,H*W,D] from
-    q, k, v and the tables, without rel_h/rel_w tensors.
-
-    workspace: "auto" (default) uses a scratch workspace cached per (device,
-    stream) until release_workspaces(); a uint8 device tensor of at least
-    fused_workspace_bytes() is used as given.
-    """
-    lib = _load()
+def _fused_operands(q, k, v, rel_pos_h, rel_pos_w, H, W, out, out_dtype):
     B, nh, D = _dims(q, H, W)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -270,6 +264,20 @@ def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_
     _need(out, "out")
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
+    return B, nh, D, out
+
+
+def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_dtype=torch.float32,
+                      workspace="auto"):
+    """relpos_build and relpos_attn_fwd in one launch: out [B,heads,H*W,D] from
+    q, k, v and the tables, without rel_h/rel_w tensors.
+
+    workspace: "auto" (default) uses a scratch workspace cached per (device,
+    stream) until release_workspaces(); a uint8 device tensor of at least
+    fused_workspace_bytes() is used as given.
+    """
+    lib = _load()
+    B, nh, D, out = _fused_operands(q, k, v, rel_pos_h, rel_pos_w, H, W, out, out_dtype)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError('workspace must be "auto" or a tensor')
@@ -281,4 +289,18 @@ def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_
                                B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     _check("relpos_attn_fused", st)
+    return out
+
+
+def relpos_attn_fused_noalloc(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out):
+    """relpos_attn_fused on the library's fixed per-device scratch array: the
+    call allocates nothing (out must be given).  Calls that may overlap on one
+    device (several streams or threads) race on the shared array."""
+    lib = _load()
+    if out is None:
+        raise ValueError("out must be given: relpos_attn_fused_noalloc allocates nothing")
+    B, nh, D, out = _fused_operands(q, k, v, rel_pos_h, rel_pos_w, H, W, out, None)
+    st = lib.relpos_attn_fused_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(out),
+                                       B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype], _stream(q))
+    _check("relpos_attn_fused_noalloc", st)
     return out

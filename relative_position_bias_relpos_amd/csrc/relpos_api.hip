@@ -133,6 +133,40 @@ int device_props(DeviceProps* out) {
   return 0;
 }
 
+// Scratch memory of relpos_attn_fused_noalloc: one array per device (each
+// device that loads the library holds its own copy until the process ends).
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory); it passes the device address looked up once
+// per device by scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[RELPOS_SCRATCH_BYTES];
+
+// Device address of the current device's scratch array, or nullptr if the
+// lookup fails (the HIP error is cleared).  Looked up on the first call on
+// each device, with that device current.
+void* scratch_ptr() {
+  static std::once_flag once[kMaxDevices];
+  static void* ptrs[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    ptrs[dev] = p;
+  });
+  return ptrs[dev];
+}
+
+relpos_status fused_impl(const void* q, const void* k, const void* v, const void* rel_pos_h,
+                         const void* rel_pos_w, void* out, int64_t B, int64_t heads, int64_t H, int64_t W,
+                         int64_t D, float scale, relpos_dtype in_dtype, relpos_dtype out_dtype, void* workspace,
+                         int64_t workspace_bytes, bool from_scratch, void* stream);
+
 // Attention configuration for B*heads = BH problems on an H x W grid on `cus`
 // compute units: 0 (8-wave workgroups), 1 (4-wave) or, when a workspace is
 // available, kAttnSplitConfig.  The cost model is the one documented with
@@ -366,6 +400,29 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
                                 int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
                                 float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
                                 void* workspace, int64_t workspace_bytes, void* stream) {
+  return fused_impl(q, k, v, rel_pos_h, rel_pos_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
+                    workspace, workspace_bytes, false, stream);
+}
+
+relpos_status relpos_attn_fused_noalloc(const void* q, const void* k, const void* v,
+                                        const void* rel_pos_h, const void* rel_pos_w, void* out,
+                                        int64_t B, int64_t heads, int64_t H, int64_t W, int64_t D,
+                                        float scale, relpos_dtype in_dtype, relpos_dtype out_dtype,
+                                        void* stream) {
+  return fused_impl(q, k, v, rel_pos_h, rel_pos_w, out, B, heads, H, W, D, scale, in_dtype, out_dtype,
+                    nullptr, 0, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// relpos_attn_fused, with the caller's workspace or (from_scratch) the
+// library's per-device scratch array.
+relpos_status fused_impl(const void* q, const void* k, const void* v, const void* rel_pos_h,
+                         const void* rel_pos_w, void* out, int64_t B, int64_t heads, int64_t H, int64_t W,
+                         int64_t D, float scale, relpos_dtype in_dtype, relpos_dtype out_dtype, void* workspace,
+                         int64_t workspace_bytes, bool from_scratch, void* stream) {
   int64_t BH = 0;
   relpos_status st = check_dims(B, heads, H, W, D, &BH);
   if (st != RELPOS_OK) return st;
@@ -387,7 +444,9 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
       {out, out_bytes},
       {workspace, 0},
   };
-  if ((st = check_align(ops, 7)) != RELPOS_OK) return st;
+  // The scratch array is not the caller's: only the six operands are checked.
+  const int nops = from_scratch ? 6 : 7;
+  if ((st = check_align(ops, nops)) != RELPOS_OK) return st;
   for (int i = 0; i < 5; ++i) {
     if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
   }
@@ -395,16 +454,21 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
   DeviceProps props{};
   if (device_props(&props) != 0) return RELPOS_E_HIP;
   const size_t need = relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W), props.cus);
-  if (static_cast<uint64_t>(workspace_bytes) < need) return RELPOS_E_SHAPE;
-  ops[6].bytes = need;
-  for (int i = 0; i < 6; ++i) {
-    if (overlaps(ops[6], ops[i])) return RELPOS_E_ALIAS;
+  if (from_scratch) {
+    if (need > static_cast<size_t>(RELPOS_SCRATCH_BYTES)) return RELPOS_E_SHAPE;
+    if ((workspace = scratch_ptr()) == nullptr) return RELPOS_E_HIP;
+  } else {
+    if (static_cast<uint64_t>(workspace_bytes) < need) return RELPOS_E_SHAPE;
+    ops[6].bytes = need;
+    for (int i = 0; i < 6; ++i) {
+      if (overlaps(ops[6], ops[i])) return RELPOS_E_ALIAS;
+    }
   }
   if (relpos::attn_lds_bytes(relpos::kAttnSplitConfig, static_cast<int>(H), static_cast<int>(W)) >
       static_cast<size_t>(props.lds_limit)) {
     return RELPOS_E_SHAPE;
   }
-  if ((st = check_device(ops, 7)) != RELPOS_OK) return st;
+  if ((st = check_device(ops, nops)) != RELPOS_OK) return st;
 
   relpos::AttnArgs a{q, k, v, nullptr, nullptr, out,
                      static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
@@ -417,6 +481,10 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
   if (relpos::launch_attn_fused(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
   return RELPOS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 relpos_status relpos_attn_fwd_ws(const void* q, const void* k, const void* v,
                                  const float* rel_h, const float* rel_w, void* out,

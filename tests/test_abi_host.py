@@ -399,3 +399,51 @@ def test_fused_pointer_errors(lib):
     p = list(base)
     p[5] = p[3]  # out over rel_pos_h
     assert _fused(lib, ptrs=p) == E_ALIAS
+
+
+# ---- relpos_attn_fused_noalloc (host-side checks) ----------------------------------
+
+def _noalloc(lib, ptrs=None, B=1, nh=2, H=4, W=4, D=64, scale=0.125, ind=BF16, outd=FP32):
+    f = lib.relpos_attn_fused_noalloc
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    p = ptrs or P
+    return f(*[vp(x) if x is not None else vp(0) for x in p[:6]], B, nh, H, W, D, scale, ind, outd, vp(0))
+
+
+def _scratch_bytes():
+    text = open(HEADER).read()
+    m = re.search(r"#define RELPOS_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_scratch_size_covers_the_workloads(lib):
+    # 96 MiB holds relpos_attn_fused's workspace on 256 CUs whenever
+    # roundup(H, 4) + roundup(W, 16) <= 252: the 64x64, 48x80 and 96x96 grids.
+    cap = _scratch_bytes()
+    assert cap == 96 << 20
+    for H, W in ((64, 64), (48, 80), (96, 96), (14, 14), (92, 160)):
+        assert _fused_ws(lib, 1, 1, H, W, BF16) <= cap, (H, W)
+    for H, W in ((128, 128), (92, 176)):
+        assert _fused_ws(lib, 1, 1, H, W, BF16) > cap, (H, W)
+
+
+def test_noalloc_argument_errors(lib):
+    # the checks of relpos_attn_fused, in its order, before any device query
+    assert _noalloc(lib, D=32) == E_SHAPE
+    assert _noalloc(lib, H=0) == E_SHAPE
+    assert _noalloc(lib, ind=FP32) == E_DTYPE
+    assert _noalloc(lib, ind=BF16, outd=FP16) == E_DTYPE
+    assert _noalloc(lib, scale=float("inf")) == E_VALUE
+    assert _noalloc(lib, ptrs=[None] * 6, B=0) == OK
+    for i in range(6):
+        p = list(P)
+        p[i] = None
+        assert _noalloc(lib, ptrs=p) == E_NULL, i
+        p = list(P)
+        p[i] += 4
+        assert _noalloc(lib, ptrs=p) == E_ALIGN, i
+    p = list(P)
+    p[5] = p[1]  # out == k
+    assert _noalloc(lib, ptrs=p) == E_ALIAS
