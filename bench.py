@@ -135,21 +135,17 @@ def dense_sdpa_context(w, q, k, v, rel_h, rel_w, ours, out, rounds=3):
         return {"kind": "context: dense bias + torch SDPA", "unavailable": f"{type(e).__name__}: {e}"[:200]}
 
 
-class ClockSampler:
-    """Polls the graphics and memory clocks (MHz) of the GPU torch uses, from
-    amdsmi, in a background thread while the GPU works; reports the samples'
-    median, min and max per phase.  Best effort: where amdsmi is missing or
-    not permitted, it reports why and the bench goes on."""
+class Clocks:
+    """Graphics/memory clock and socket power of the GPU torch uses, read from
+    the SMU metrics table through amdsmi.  The table is refreshed about once a
+    second, so a reading reflects the last second or so: readings are taken
+    after at least a second of sustained load.  Best effort: where amdsmi is
+    missing or not permitted, the reason is reported and the bench goes on."""
 
-    def __init__(self, dev_index=0, period_s=0.002):
-        import threading
-        self.period = period_s
-        self.samples = {}
-        self.phase = None
-        self.error = None
-        self._stop = threading.Event()
-        self._lock = threading.Lock()
+    def __init__(self, dev_index=0):
         self.handle = None
+        self.error = None
+        self.readings = {}
         try:
             import amdsmi
             import torch
@@ -166,38 +162,27 @@ class ClockSampler:
                         break
                 except Exception:
                     pass
-            self.read()
         except Exception as e:
             self.error = f"{type(e).__name__}: {e}"[:120]
             self.handle = None
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        self._thread.start()
 
-    def read(self):
-        g = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
-        m = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.MEM)
-        return g.get("clk"), m.get("clk"), g.get("max_clk")
-
-    def _run(self):
-        while not self._stop.is_set():
-            if self.handle is not None and self.phase is not None:
-                try:
-                    sclk, mclk, smax = self.read()
-                    with self._lock:
-                        self.samples.setdefault(self.phase, []).append((sclk, mclk))
-                        self.sclk_max = smax
-                except Exception as e:
-                    self.error = f"{type(e).__name__}: {e}"[:120]
-            time.sleep(self.period)
-
-    def set_phase(self, name):
-        with self._lock:
-            self.phase = name
+    def read(self, label):
+        if self.handle is None:
+            return
+        try:
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            per_xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
+            num = lambda x: x if isinstance(x, (int, float)) else None
+            self.readings[label] = {
+                "gfxclk_mhz": num(m.get("current_gfxclk")),
+                "gfxclk_per_xcd_mhz": per_xcd or None,
+                "uclk_mhz": num(m.get("current_uclk")),
+                "socket_power_w": num(m.get("current_socket_power")),
+            }
+        except Exception as e:
+            self.error = f"{type(e).__name__}: {e}"[:120]
 
     def report(self):
-        import statistics
-        self._stop.set()
-        self._thread.join(timeout=1.0)
         try:
             if self.handle is not None:
                 self.amdsmi.amdsmi_shut_down()
@@ -205,13 +190,10 @@ class ClockSampler:
             pass
         if self.handle is None:
             return {"unavailable": self.error}
-        out = {"sclk_max_mhz": getattr(self, "sclk_max", None), "period_ms": self.period * 1e3}
-        for ph, xs in self.samples.items():
-            sc = [x[0] for x in xs if x[0] is not None]
-            mc = [x[1] for x in xs if x[1] is not None]
-            if sc:
-                out[ph] = {"n": len(sc), "sclk_median_mhz": statistics.median(sc), "sclk_min_mhz": min(sc),
-                           "sclk_max_mhz": max(sc), "mclk_median_mhz": statistics.median(mc) if mc else None}
+        out = {"source": "amdsmi SMU metrics table (refreshed about once a second)", "gfxclk_max_mhz": 2400}
+        out.update(self.readings)
+        if self.error:
+            out["error"] = self.error
         return out
 
 
@@ -245,7 +227,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed ones")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
+    ap.add_argument("--rounds", type=int, default=5, help="rounds of the per-call measurements")
+    ap.add_argument("--calls-per-round", type=int, default=20, help="back-to-back calls per round and kind")
+    ap.add_argument("--settle-ms", type=float, default=1200.0,
                     help="untimed back-to-back steps for this long (wall clock) before the warm-up, so the "
                          "GPU clock has ramped up; recorded in the output line")
     ap.add_argument("--workload", default="deepencoder")
@@ -262,8 +246,8 @@ def main():
               "(every (batch, head) is independent; see DESIGN.md for how it would shard).",
               file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.rounds < 1 or args.calls_per_round < 1:
+        print("--steps, --rounds and --calls-per-round must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -309,8 +293,38 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    clk = ClockSampler()
-    clk.set_phase("settle")
+    # C calls with their arguments marshalled once, for the per-call loops
+    # (the Python binding's own cost, about 11 us a call, would otherwise bound
+    # the shorter calls); they run the same C entry points as the binding.
+    lib = rp._load()
+    stream = rp._stream(q)
+    common = (w.B, w.heads, H, W, w.D)
+    c_build = (rp._ptr(q), rp._ptr(th), rp._ptr(tw), rp._ptr(rel_h), rp._ptr(rel_w), *common,
+               rp._DT[q.dtype], stream)
+    c_attn = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(rel_h), rp._ptr(rel_w), rp._ptr(out), *common,
+              float(scale), rp._DT[q.dtype], rp._DT[out.dtype], stream)
+    c_fused = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(th), rp._ptr(tw), rp._ptr(out_fused), *common,
+               float(scale), rp._DT[q.dtype], rp._DT[out_fused.dtype], rp._ptr(ws_fused), ws_fused.numel(), stream)
+    per_call = {
+        "attn": lambda: lib.relpos_attn_fwd(*c_attn),
+        "build": lambda: lib.relpos_build(*c_build),
+        "fused": lambda: lib.relpos_attn_fused(*c_fused),
+    }
+
+    def region(fn, n):
+        """n back-to-back calls between two HIP events on the launch stream
+        (torch's current stream, which every call here is given): ms per call."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    clk = Clocks(dev.index or 0)
+    clk.read("idle")
     # Clock settle: back-to-back steps (and fused calls) for --settle-ms of wall
     # time, synchronised every 20 so the queue stays short.
     settle_calls = 0
@@ -325,36 +339,27 @@ def main():
         step()
         fused()
     torch.cuda.synchronize()
+    clk.read("end_of_settle")
     mem_before = torch.cuda.memory_allocated()
-    clk.set_phase("timed")
 
-    # Timed region: exactly K steps bracketed by synchronisations; HIP events
-    # on the launch stream (torch's current stream, which the binding passes)
-    # before the build, between the two calls and after the attention call.
+    # Timed region: exactly K steps through the Python binding, back to back,
+    # bracketed by synchronisations and one HIP event on each side.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record()
-        build()
-        ev[i][1].record()
-        attn()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    ms_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
-    build_calls = [e[0].elapsed_time(e[1]) for e in ev]
-    attn_calls = [e[1].elapsed_time(e[2]) for e in ev]
-    clk.set_phase(None)
+    ms_step = region(step, K)
 
-    # The fused call, timed the same way in its own loop.
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    # Per-call figures: R rounds, each with `n` back-to-back calls of every
+    # kind in turn (attention, build, fused); a round's time / n is one sample.
+    R, n = args.rounds, args.calls_per_round
+    samples = {name: [] for name in per_call}
+    for _ in range(R):
+        for name, fn in per_call.items():
+            samples[name].append(region(fn, n))
+    clk.read("after_timed")
+    attn_calls, build_calls, fused_calls = samples["attn"], samples["build"], samples["fused"]
+    for name, fn in per_call.items():
+        if fn() != 0:
+            raise RuntimeError(f"{name} call failed")
     torch.cuda.synchronize()
-    for i in range(K):
-        fev[i][0].record()
-        fused()
-        fev[i][1].record()
-    torch.cuda.synchronize()
-    fused_calls = [e[0].elapsed_time(e[1]) for e in fev]
     mem_after = torch.cuda.memory_allocated()
 
     # Host cost of one attention call (binding + argument checks + launch),
@@ -367,18 +372,15 @@ def main():
         attn()
     host_us = (time.perf_counter() - t0) / n_host * 1e6
     torch.cuda.synchronize()
-    lib = rp._load()
-    cargs = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(rel_h), rp._ptr(rel_w), rp._ptr(out),
-             w.B, w.heads, H, W, w.D, float(scale), rp._DT[q.dtype], rp._DT[out.dtype], rp._stream(q))
     t0 = time.perf_counter()
     for _ in range(n_host):
-        lib.relpos_attn_fwd(*cargs)
+        per_call["attn"]()
     c_us = (time.perf_counter() - t0) / n_host * 1e6
     torch.cuda.synchronize()
 
-    attn_ms = sum(attn_calls) / K
-    build_ms = sum(build_calls) / K
-    fused_ms = sum(fused_calls) / K
+    attn_ms = sum(attn_calls) / R
+    build_ms = sum(build_calls) / R
+    fused_ms = sum(fused_calls) / R
 
     # Output check on sampled rows of the last call (two heads) against the oracle
     # is left to the test-suite; here only finiteness is asserted.
@@ -422,8 +424,11 @@ def main():
         "build_ms_per_call": round(build_ms, 5),
         "build_ms_per_call_stats": stats_ms(build_calls),
         "build_gbs": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
-        "timing": "HIP events on the launch stream around every call of the timed steps; "
-                  "ms_per_step = first event to last / steps; *_ms_per_call = mean of the per-call events",
+        "timing": "ms_per_step: the K steps back to back through the Python binding, one HIP event on "
+                  "each side (launch stream); *_ms_per_call: R rounds of n back-to-back C calls of each "
+                  "kind in turn, one event pair per round, a sample = round time / n; mean over all calls, "
+                  "median/min/max over the rounds",
+        "rounds": {"R": R, "calls_per_round": n},
         "settle": {"ms": args.settle_ms, "calls": settle_calls,
                    "what": "untimed back-to-back steps and fused calls before the warm-up (clock ramp)"},
         "clocks": clk.report(),

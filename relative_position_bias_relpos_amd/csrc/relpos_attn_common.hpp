@@ -34,24 +34,6 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Raw buffer loads: an offset at or past the resource's byte size returns
-// zeros in hardware, which masks grid cells outside the tile without branches.
-constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw-buffer descriptor word 3
-constexpr int kOob = 0x7ffffff0;             // any offset past every resource used here
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                          static_cast<int>(kBufFlags));
-}
-// `soff` is a wave-uniform byte offset (scalar register); callers that rely
-// on the zero fill keep it 0 and put the whole offset in `off`.
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
-}
-__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
-}
-
 // Logical work index of this workgroup.  Workgroups are dispatched round-robin
 // over the 8 XCDs; this maps the blocks that land on one XCD to a contiguous
 // range of (head, query tile) work so that a head's K/V stays in one XCD's L2.

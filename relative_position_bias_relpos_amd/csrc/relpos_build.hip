@@ -2,15 +2,29 @@
 // (PR #55629 page, key source snippet, the add_decomposed_rel_pos call on the
 // unscaled q; table index qh - kh + H - 1, resp. qw - kw + W - 1).
 //
-// For a fixed query grid row qh the W queries of that row all use the same
-// window of H table rows, reversed: rel_h[qh*W + m, n] = q[qh*W + m] . T_h[qh - n + H - 1].
-// That is a [W x 64] x [64 x H] product, done here with 32x32x16 MFMA (bf16 or
-// fp16 products are exact in fp32, accumulation is fp32).  rel_w is the same
-// with the roles of the axes swapped: for a fixed grid column qw, the H queries
-// m*W + qw against T_w[qw - n + W - 1].
+// The kernel writes 8 bytes of bias per byte of q it reads (D = 64, H + W
+// fp32 values per query against 64 bf16/fp16 values), so it is bound by HBM
+// writes.  Each q row is read once for both axes, and every output goes out
+// in 16-byte stores over contiguous rows.
 //
-// Grid: x = H + W (one workgroup per grid row, then per grid column), y = B*heads.
-// The waves of a workgroup share out its 32x32 output tiles.
+// A workgroup is one wave and owns a unit of up to 32 consecutive queries of
+// one grid row qh (columns qw = m0 .. m0 + 31):
+//   * rel_h: all queries of the unit use the same table rows, reversed:
+//     rel_h[m, kh] = q[m] . T_h[qh - kh + H - 1], a [32 x 64] x [64 x H]
+//     product on 32x32x16 MFMA (bf16/fp16 products are exact in fp32,
+//     accumulation is fp32), 64 columns at a time.
+//   * rel_w: the table row depends on qw - kw, so for 64 output columns
+//     kw = n0 .. n0 + 63 the wave forms G[m', j] = q[m0 + m'] . T_w[tlo + j]
+//     over the 95 table rows tlo .. tlo + 94 those columns reach (tlo = m0 -
+//     n0 - 63 + W - 1), i.e. 96 columns of MFMA output, and reads the output
+//     back along the diagonal: rel_w[m0 + m', n0 + n'] = G[m', m' - n' + 63].
+// Either product is staged in LDS (row strides of 72 and 104 floats, which
+// put the two 32-lane halves of an MFMA result store on disjoint banks) and
+// stored as rows of 16-byte pieces.  All loads are branch-free raw buffer
+// loads (zeros past a tensor's end), so a chunk's q and table loads are in
+// flight together and the next chunk's are issued before this one's stores.
+//
+// Grid: x = H * ceil(W / 32) units of one (b, h), y = B*heads.
 #include "relpos_device.hpp"
 #include "relpos_kernels.hpp"
 
@@ -19,69 +33,146 @@ namespace relpos {
 namespace {
 
 constexpr int kD = 64;
+constexpr int kHStride = 72;   // floats per staged rel_h row (64 used)
+constexpr int kGStride = 104;  // floats per staged G row (95 used)
+
+// 16 bytes of output: 4 consecutive floats of one row from column n (a
+// multiple of 4) on, the part below `cols` (a row's length) written; one
+// 16-byte store where the rows keep 16-byte alignment (cols % 4 == 0, the
+// tensors being 16-byte aligned), else one store per float.
+__device__ __forceinline__ void store_row4(float* dst, int n, int cols, f32x4 v) {
+  if ((cols & 3) == 0 && n < cols) {
+    *reinterpret_cast<f32x4*>(dst + n) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n + e < cols) dst[n + e] = v[e];
+    }
+  }
+}
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void build_kernel(const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ th,
-                                                    const uint16_t* __restrict__ tw,
-                                                    float* __restrict__ rel_h,
-                                                    float* __restrict__ rel_w, int H, int W) {
-  const int N = H * W;
-  const size_t head = static_cast<size_t>(blockIdx.y) * N;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
+__global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ th,
+                                                   const uint16_t* __restrict__ tw,
+                                                   float* __restrict__ rel_h,
+                                                   float* __restrict__ rel_w, int H, int W, int mtn) {
+  __shared__ __attribute__((aligned(16))) float stage_h[32 * kHStride];
+  __shared__ __attribute__((aligned(16))) float stage_g[32 * kGStride];
+  const int lane = threadIdx.x;
+  const int ml = lane & 31, half = lane >> 5;
+  const int qh = blockIdx.x / mtn;
+  const int m0 = (blockIdx.x - qh * mtn) * 32;
+  const int rows = W - m0 < 32 ? W - m0 : 32;
+  const size_t row0 = static_cast<size_t>(blockIdx.y) * H * W + static_cast<size_t>(qh) * W + m0;
 
-  // Problem for this workgroup: rows m < M are queries (base + m*stride),
-  // columns n < NC index the output axis, table row = tbase - n.
-  int M, NC, base, stride, tbase, ldo;
-  const uint16_t* tab;
-  float* dst;
-  if (static_cast<int>(blockIdx.x) < H) {
-    const int qh = blockIdx.x;
-    M = W; NC = H; base = qh * W; stride = 1; tbase = qh + H - 1; tab = th; dst = rel_h; ldo = H;
-  } else {
-    const int qw = blockIdx.x - H;
-    M = H; NC = W; base = qw; stride = W; tbase = qw + W - 1; tab = tw; dst = rel_w; ldo = W;
+  // Every load is a raw buffer load whose out-of-range offsets read zeros:
+  // no branch, so all of a chunk's loads are in flight together.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row0 * kD, static_cast<uint32_t>(rows) * kD * 2);
+  const __amdgpu_buffer_rsrc_t rth = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+  const __amdgpu_buffer_rsrc_t rtw = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+  const int dchunk = 16 * half;  // byte offset of this lane's 8 d values within a 16-wide slice
+
+  // A operand: query m0 + ml, d = 16*kd + 8*half .. +7
+  u32x4 a[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml < rows ? ml * kD * 2 + 32 * kd + dchunk : kOob);
+
+  // B operands: table row per output column (rel_h) or per G column (rel_w)
+  u32x4 bh[2][4], bw[3][4];
+  auto load_h = [&](int n0) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int kh = n0 + 32 * nt + ml;
+      const int off = kh < H ? (qh - kh + H - 1) * kD * 2 + dchunk : kOob;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) bh[nt][kd] = buf_load16(rth, off, 32 * kd);
+    }
+  };
+  auto load_w = [&](int n0) {
+    const int tlo = m0 - n0 - 63 + W - 1;
+#pragma unroll
+    for (int gt = 0; gt < 3; ++gt) {
+      const int t = tlo + 32 * gt + ml;
+      const int off = t >= 0 && t <= 2 * W - 2 ? t * kD * 2 + dchunk : kOob;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) bw[gt][kd] = buf_load16(rtw, off, 32 * kd);
+    }
+  };
+  load_h(0);
+  load_w(0);
+
+  // MFMA output register r of this lane: row 8*(r/4) + 4*half + r%4, column ml.
+  auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
+  // Store pass: lane covers columns sc .. sc+3 of rows lane/16 + 4i.
+  const int sc = 4 * (lane & 15);
+  const int sr = lane >> 4;
+
+  // ---- rel_h --------------------------------------------------------------------
+  for (int n0 = 0; n0 < H; n0 += 64) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 acc{};
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) acc = mfma32<BF16>(a[kd], bh[nt][kd], acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage_h[out_row(r) * kHStride + 32 * nt + ml] = acc[r];
+    }
+    if (n0 + 64 < H) load_h(n0 + 64);
+    __syncthreads();
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4*>(stage_h + (sr + 4 * i) * kHStride + sc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      if (m < rows) store_row4(rel_h + (row0 + m) * H, n0 + sc, H, v[i]);
+    }
+    __syncthreads();
   }
-  const int mt_n = (M + 31) / 32, nt_n = (NC + 31) / 32;
 
-  for (int tile = wave; tile < mt_n * nt_n; tile += 4) {
-    const int mt = tile / nt_n, nt = tile - mt * nt_n;
-    const int m = mt * 32 + (lane & 31);
-    const int n = nt * 32 + (lane & 31);
-    const bool mok = m < M, nok = n < NC;
-    const uint16_t* qrow = q + (head + base + static_cast<size_t>(m) * stride) * kD;
-    const uint16_t* trow = tab + static_cast<size_t>(nok ? tbase - n : 0) * kD;
-    f32x16 acc{};
+  // ---- rel_w --------------------------------------------------------------------
+  for (int n0 = 0; n0 < W; n0 += 64) {
 #pragma unroll
-    for (int kd = 0; kd < 4; ++kd) {
-      const u32x4 a = mok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kd + 8 * half) : u32x4{0, 0, 0, 0};
-      const u32x4 b = nok ? *reinterpret_cast<const u32x4*>(trow + 16 * kd + 8 * half) : u32x4{0, 0, 0, 0};
-      acc = mfma32<BF16>(a, b, acc);
-    }
-    if (nok) {
+    for (int gt = 0; gt < 3; ++gt) {
+      f32x16 g{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mr = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (mr < M) dst[(head + base + static_cast<size_t>(mr) * stride) * ldo + n] = acc[r];
-      }
+      for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], bw[gt][kd], g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage_g[out_row(r) * kGStride + 32 * gt + ml] = g[r];
     }
+    if (n0 + 64 < W) load_w(n0 + 64);
+    __syncthreads();
+    // columns n0 + sc + e of row m take G[m, m - sc - e + 63]
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      const float* gp = stage_g + m * kGStride + m - sc + 63;
+      v[i] = f32x4{gp[0], gp[-1], gp[-2], gp[-3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      if (m < rows) store_row4(rel_w + (row0 + m) * W, n0 + sc, W, v[i]);
+    }
+    __syncthreads();
   }
 }
 
 }  // namespace
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.H + a.W), static_cast<unsigned>(a.BH));
+  const int mtn = (a.W + 31) / 32;
+  dim3 grid(static_cast<unsigned>(a.H * mtn), static_cast<unsigned>(a.BH));
   if (a.bf16) {
-    hipLaunchKernelGGL(build_kernel<true>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL(build_kernel<true>, grid, dim3(64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.rel_pos_h),
-                       static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W);
+                       static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W, mtn);
   } else {
-    hipLaunchKernelGGL(build_kernel<false>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL(build_kernel<false>, grid, dim3(64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.rel_pos_h),
-                       static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W);
+                       static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W, mtn);
   }
   return hipGetLastError();
 }

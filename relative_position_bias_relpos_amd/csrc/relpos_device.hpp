@@ -64,6 +64,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer loads: an offset at or past the resource's byte size returns
+// zeros in hardware, which masks grid cells outside the tile without branches.
+constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw-buffer descriptor word 3
+constexpr int kOob = 0x7ffffff0;             // any offset past every resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                          static_cast<int>(kBufFlags));
+}
+// `soff` is a wave-uniform byte offset (scalar register); callers that rely
+// on the zero fill keep it 0 and put the whole offset in `off`.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+
 }  // namespace relpos
 
 namespace relpos {
