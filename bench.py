@@ -10,6 +10,7 @@ kernel) is timed beside it.  Prints ONE JSON line.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -227,6 +228,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed ones")
+    ap.add_argument("--attn-config", type=int, default=-1,
+                    help="force this launch configuration of relpos_attn_fwd (relpos_attn_fwd_cfg; -1: the "
+                         "library's own choice, the default) to measure the configurations against each other")
     ap.add_argument("--rounds", type=int, default=5, help="rounds of the per-call measurements")
     ap.add_argument("--calls-per-round", type=int, default=20, help="back-to-back calls per round and kind")
     ap.add_argument("--settle-ms", type=float, default=1200.0,
@@ -270,8 +274,10 @@ def main():
     def build():
         rp.relpos_build(q, th, tw, H, W, rel_h=rel_h, rel_w=rel_w)
 
+    cfg = None if args.attn_config < 0 else args.attn_config
+
     def attn():
-        rp.relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=out)
+        rp.relpos_attn_fwd(q, k, v, rel_h, rel_w, H, W, scale, out=out, config=cfg)
 
     def step():
         build()
@@ -302,11 +308,14 @@ def main():
     c_build = (rp._ptr(q), rp._ptr(th), rp._ptr(tw), rp._ptr(rel_h), rp._ptr(rel_w), *common,
                rp._DT[q.dtype], stream)
     c_attn = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(rel_h), rp._ptr(rel_w), rp._ptr(out), *common,
-              float(scale), rp._DT[q.dtype], rp._DT[out.dtype], stream)
+              float(scale), rp._DT[q.dtype], rp._DT[out.dtype])
+    c_attn = (c_attn + (stream,) if cfg is None
+              else c_attn + (ctypes.c_int(cfg), ctypes.c_void_p(0), 0, stream))
+    attn_c = lib.relpos_attn_fwd if cfg is None else lib.relpos_attn_fwd_cfg
     c_fused = (rp._ptr(q), rp._ptr(k), rp._ptr(v), rp._ptr(th), rp._ptr(tw), rp._ptr(out_fused), *common,
                float(scale), rp._DT[q.dtype], rp._DT[out_fused.dtype], rp._ptr(ws_fused), ws_fused.numel(), stream)
     per_call = {
-        "attn": lambda: lib.relpos_attn_fwd(*c_attn),
+        "attn": lambda: attn_c(*c_attn),
         "build": lambda: lib.relpos_build(*c_build),
         "fused": lambda: lib.relpos_attn_fused(*c_fused),
     }
@@ -416,6 +425,9 @@ def main():
             "B": w.B, "heads": w.heads, "H": H, "W": W, "D": w.D, "seq_len": w.N,
             "global_batch": w.B, "parallelism": "none (1 GPU)",
         },
+        "attn_launch_config": (cfg if cfg is not None else
+                               rp.attn_config(w.B, w.heads, H, W, q.dtype,
+                                              torch.cuda.get_device_properties(dev).multi_processor_count)),
         "attn_ms_per_call": round(attn_ms, 5),
         "attn_ms_per_call_stats": stats_ms(attn_calls),
         "attn_tflops": round(attn_tflops, 2),

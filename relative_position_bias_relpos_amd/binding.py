@@ -83,7 +83,8 @@ def abi_version():
 def attn_config(B, heads, H, W, dtype, cu_count, with_workspace=False):
     """Launch configuration the attention call uses for this problem on a
     device with `cu_count` compute units (0: 8-wave workgroups, 1: 4-wave,
-    3: 16-query waves, 5: key range split, only with a workspace); host-only."""
+    3: 16-query waves, 5: key range split, only with a workspace, 6: 12-wave
+    workgroups of 192 queries); host-only."""
     c = _load().relpos_attn_config(int(B), int(heads), int(H), int(W), _DT[dtype], int(cu_count),
                                    1 if with_workspace else 0)
     if c < 0:

@@ -51,6 +51,11 @@ constexpr int kSlotBytes12 = 2 * kPairBytes12;     // one pair per head spanned
 constexpr int kRawBytes12 = 2 * 2 * kTileBytes12;   // V of a pair as loaded, per head (before conversion)
 constexpr int kLds12 = 2 * kSlotBytes12 + kRawBytes12;  // two slots + the raw V area: 160 KB
 constexpr int kMergeStride12 = 64 * 16 * 4 + 2 * 32 * 4;  // per wave: 16 accumulators per lane, m, l
+// Output staging after the merge, per wave: its 32 queries x 32 d (fp32), rows
+// padded to 36 floats; placed after the 12 merge areas.
+constexpr int kOutStride12 = 36;
+constexpr int kOutBase12 = kWaves12 * kMergeStride12;
+static_assert(kOutBase12 + kWaves12 * 32 * kOutStride12 * 4 <= kLds12, "output staging must fit the LDS");
 // bf16 inputs with at least this many keys run P.V in bf16.  Rounding p to
 // bf16 (8 significant bits) adds to each output an error that averages out
 // over the keys; emulated in float64 on the workloads here, its mean over
@@ -551,19 +556,38 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   const float wa = exp2_fast(m - mx), wb = exp2_fast(mp - mx);
   const float inv = 1.0f / (lt * wa + lp * wb);
   const float ca = wa * inv, cb = wb * inv;
-  if (!bvalid || !qok) return;
+  // This wave's output columns 32*par .. 32*par + 31 of its 32 queries go
+  // through LDS (query-major) so that every store writes whole rows of 32
+  // values: 128-byte (fp32) or 64-byte (half) pieces, not 16- or 8-byte ones
+  // that would reach memory as partial lines.
+  float* ostage = reinterpret_cast<float*>(smem + kOutBase12) + wave * 32 * kOutStride12;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int d = 32 * par + 8 * g + 4 * half;
     f32x4 o4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o4[e] = acc[par][4 * g + e] * ca + theirs[(4 * g + e) * 64 + lane] * cb;
-    if constexpr (OUT_F32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (head + qi) * kD + d) = o4;
-    } else {
-      const u32x2 pk2 = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
-                             : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (head + qi) * kD + d) = pk2;
+    *reinterpret_cast<f32x4*>(ostage + ql * kOutStride12 + 8 * g + 4 * half) = o4;
+  }
+  // the rows are read back by other lanes of this wave only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (!bvalid) return;
+  const int rows_here = N - q0 < 32 ? N - q0 : 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);  // query row of the block
+    const int c = 4 * (lane & 7);       // first of this lane's 4 columns
+    const f32x4 o4 = *reinterpret_cast<const f32x4*>(ostage + r * kOutStride12 + c);
+    if (r < rows_here) {
+      const size_t at = (head + q0 + r) * kD + 32 * par + c;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + at) = o4;
+      } else {
+        const u32x2 pk2 = BF16 ? u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])}
+                               : u32x2{pack_f16(o4[0], o4[1]), pack_f16(o4[2], o4[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + at) = pk2;
+      }
     }
   }
 }
