@@ -189,22 +189,30 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
                                     relpos_dtype in_dtype, int cu_count);
 
 /*
- * relpos_attn_fused: relpos_build followed by relpos_attn_fwd in one launch,
+ * relpos_attn_fused: relpos_build followed by relpos_attn_fwd in one call,
  * without the rel_h / rel_w tensors (the fusion the PR #55629 page's
  * implementation section leaves to the model helper: there rel_h and rel_w are
  * built by add_decomposed_rel_pos before the fused kernel is called).
  *
  * Defines the same `out` as relpos_build + relpos_attn_fwd on the same inputs
  * (same tolerance against the definition; results differ from the two-call
- * path by rounding only).  Each workgroup computes the bias rows of its 256
- * queries from q and the tables on MFMA (fp32 accumulation, as relpos_build)
- * and reads them back per key tile: rel_w rows from its slot of the
- * workspace, rel_h rows from LDS when 256*(roundup(H,4)+4) floats fit beside
- * the K/V staging (H <= 72 on a 160 KB LDS), else from the slot as well.
- * The launch is the persistent split launch of relpos_attn_fwd_ws (one 8-wave
- * workgroup per compute unit, merge kernel when split) with a fixed cost of
- * 12 tiles per segment in place of 6; the last round is left whole when its
- * split would not be faster (max(s + 12, k*(T - s + 12)) + 4 >= T + 12).
+ * path by rounding only).  Two launch forms, chosen by the grid:
+ *   - bf16 inputs with W % 32 == 0, H % 4 == 0, H*W >= 1024 and at least 6
+ *     blocks of 32 queries per (b, h): the 12-wave kernel of configuration 6
+ *     on a persistent grid of min(units, CUs) workgroups (units =
+ *     ceil(B*heads*H*W/32 / 6)).  For each unit a workgroup first computes its
+ *     6 blocks' bias rows on MFMA (fp32 accumulation, the same products as
+ *     relpos_build, so the result equals the two-call path's bit for bit)
+ *     into its slot of the workspace, then runs the key loop reading them
+ *     from there.  No second kernel.
+ *   - otherwise: each workgroup of the persistent split launch of
+ *     relpos_attn_fwd_ws (one 8-wave workgroup per compute unit, merge kernel
+ *     when split) computes the bias rows of its 256 queries and reads them
+ *     back per key tile: rel_w rows from its slot of the workspace, rel_h rows
+ *     from LDS when 256*(roundup(H,4)+4) floats fit beside the K/V staging
+ *     (H <= 72 on a 160 KB LDS), else from the slot as well; a fixed cost of
+ *     12 tiles per segment in place of 6; the last round is left whole when
+ *     its split would not be faster (max(s + 12, k*(T - s + 12)) + 4 >= T + 12).
  *
  * Arguments: q, k, v, out, B, heads, H, W, D, scale, in_dtype, out_dtype and
  * stream as for relpos_attn_fwd (with the same scale rule and bf16 v range),
@@ -243,7 +251,8 @@ relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
  * Same operation, arguments (without workspace and workspace_bytes), result
  * and errors as relpos_attn_fused, plus
  *   E_SHAPE  when relpos_fused_workspace_bytes(...) for the current device
- *            exceeds RELPOS_SCRATCH_BYTES (on 256 compute units: when
+ *            exceeds RELPOS_SCRATCH_BYTES (on 256 compute units, for any
+ *            batch: with the 12-wave kernel when H + W > 512, otherwise when
  *            roundup(H, 4) + roundup(W, 16) > 252; 64x64, 48x80 and 96x96
  *            fit).
  *   E_HIP    when the scratch array's address cannot be looked up.
@@ -261,7 +270,11 @@ relpos_status relpos_attn_fused_noalloc(const void* q, const void* k, const void
 
 /*
  * relpos_fused_workspace_bytes: workspace bytes relpos_attn_fused needs on a
- * device with `cu_count` compute units:
+ * device with `cu_count` compute units.  With the 12-wave kernel (the first
+ * form above): min(units, cu_count) * 6 * 32 * (H + W) * 4, one slot of bias
+ * rows per workgroup -- at most the size of the rel_h / rel_w tensors it
+ * replaces once B*heads*H*W/192 >= cu_count (25.2 MB at 64x64 with 12 heads).
+ * Otherwise:
  *   cu_count * (2 * (256*64 + 2*256) + 256 * (roundup(H, 4) + roundup(W, 16))) * 4
  * (two split pieces and one slot of bias rows per workgroup).  -1 if a size
  * or the dtype is out of range or cu_count < 1.  Host-only.

@@ -391,6 +391,10 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
                                      int cu_count) {
   int64_t BH = 0;
   if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
+  if (relpos::attn_fused12_ok(static_cast<int>(H), static_cast<int>(W), in_dtype == RELPOS_BF16)) {
+    return static_cast<int64_t>(
+        relpos::attn_fused12_workspace_bytes(BH, static_cast<int>(H), static_cast<int>(W), cu_count));
+  }
   return static_cast<int64_t>(relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W),
                                                                  cu_count));
 }
@@ -453,7 +457,10 @@ relpos_status fused_impl(const void* q, const void* k, const void* v, const void
   // The workspace size depends on the device's compute-unit count.
   DeviceProps props{};
   if (device_props(&props) != 0) return RELPOS_E_HIP;
-  const size_t need = relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W), props.cus);
+  // The 12-wave fused kernel where the grid allows it, else the split-grid one.
+  const bool f12 = relpos::attn_fused12_ok(static_cast<int>(H), static_cast<int>(W), in_dtype == RELPOS_BF16);
+  const size_t need = f12 ? relpos::attn_fused12_workspace_bytes(BH, static_cast<int>(H), static_cast<int>(W), props.cus)
+                          : relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W), props.cus);
   if (from_scratch) {
     if (need > static_cast<size_t>(RELPOS_SCRATCH_BYTES)) return RELPOS_E_SHAPE;
     if ((workspace = scratch_ptr()) == nullptr) return RELPOS_E_HIP;
@@ -464,7 +471,8 @@ relpos_status fused_impl(const void* q, const void* k, const void* v, const void
       if (overlaps(ops[6], ops[i])) return RELPOS_E_ALIAS;
     }
   }
-  if (relpos::attn_lds_bytes(relpos::kAttnSplitConfig, static_cast<int>(H), static_cast<int>(W)) >
+  if ((f12 ? relpos::attn12_lds_bytes()
+           : relpos::attn_lds_bytes(relpos::kAttnSplitConfig, static_cast<int>(H), static_cast<int>(W))) >
       static_cast<size_t>(props.lds_limit)) {
     return RELPOS_E_SHAPE;
   }
@@ -478,7 +486,9 @@ relpos_status fused_impl(const void* q, const void* k, const void* v, const void
   a.th = rel_pos_h;
   a.tw = rel_pos_w;
   a.lds_limit = props.lds_limit;
-  if (relpos::launch_attn_fused(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+  const hipError_t err = f12 ? relpos::launch_attn_fused12(a, static_cast<hipStream_t>(stream))
+                            : relpos::launch_attn_fused(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return RELPOS_E_LAUNCH;
   return RELPOS_OK;
 }
 

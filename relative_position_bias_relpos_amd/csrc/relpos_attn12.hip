@@ -102,24 +102,110 @@ __device__ __forceinline__ void lds_load16(sgpr4 rs, int voff, int soff, uint32_
       : "memory", "m0");
 }
 
+// Bias rows of one block of 32 queries (m0 .. m0+31 of grid row qh, W % 32 ==
+// 0) for the fused call, computed by one wave on 32x32x16 MFMA: axis 0 writes
+// rel_h [32][H] at dst, axis 1 rel_w [32][W] (the same products as
+// relpos_build: rel_h against the reversed window of T_h, rel_w through the
+// 96 columns of q . T_w its 64-column chunks reach, read back along the
+// diagonal).  `stage` is this wave's LDS staging area (32 x 104 floats).
+template <bool BF16>
+__device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qrows,
+                                                const uint16_t* __restrict__ th,
+                                                const uint16_t* __restrict__ tw, float* __restrict__ dst,
+                                                int axis, int qh, int m0, int H, int W, float* stage,
+                                                int lane) {
+  constexpr int kHS = 72, kGS = 104;  // staging row strides (floats)
+  const int ml = lane & 31, half = lane >> 5;
+  const int dchunk = 16 * half;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qrows, 32 * kD * 2);
+  u32x4 a[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml * kD * 2 + 32 * kd + dchunk);
+  auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
+  const int sc = 4 * (lane & 15), sr = lane >> 4;
+  if (axis == 0) {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+    for (int n0 = 0; n0 < H; n0 += 64) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int kh = n0 + 32 * nt + ml;
+        const int off = kh < H ? (qh - kh + H - 1) * kD * 2 + dchunk : kOob;
+        f32x16 acc{};
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) acc = mfma32<BF16>(a[kd], buf_load16(rt, off, 32 * kd), acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stage[out_row(r) * kHS + 32 * nt + ml] = acc[r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = sr + 4 * i, n = n0 + sc;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(stage + m * kHS + sc);
+        if (n < H) *reinterpret_cast<f32x4*>(dst + m * H + n) = x;  // H % 4 == 0 here
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+    for (int n0 = 0; n0 < W; n0 += 64) {
+      const int tlo = m0 - n0 - 63 + W - 1;
+#pragma unroll
+      for (int gt = 0; gt < 3; ++gt) {
+        const int t = tlo + 32 * gt + ml;
+        const int off = t >= 0 && t <= 2 * W - 2 ? t * kD * 2 + dchunk : kOob;
+        f32x16 g{};
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], buf_load16(rt, off, 32 * kd), g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stage[out_row(r) * kGS + 32 * gt + ml] = g[r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = sr + 4 * i, n = n0 + sc;
+        const float* gp = stage + m * kGS + m - sc + 63;  // G[m, m - (sc + e) + 63]
+        const f32x4 x{gp[0], gp[-1], gp[-2], gp[-3]};
+        if (n < W) *reinterpret_cast<f32x4*>(dst + 32 * H + m * W + n) = x;  // W % 32 == 0 here
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+// One unit (6 blocks of 32 queries) of the 12-wave kernel.
 // PB (bf16 inputs only): P.V runs in bf16 (P rounded to bf16, V staged as
 // loaded); otherwise in fp16 (bf16 V converted to fp16 while staged).
-template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB>
-__global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
+// FUSED: the bias rows of the unit's blocks are computed first into this
+// workgroup's slot of `ws` (block b: rel_h [32][H] then rel_w [32][W] at
+// b * 32 * (H + W) floats) and read from there instead of rel_h / rel_w.
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB, bool FUSED>
+__device__ __forceinline__ void attn12_unit(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int nblk, int total_blocks, float c2, float rw_mul, int zero_q) {
+    const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw, float* __restrict__ ws,
+    int H, int W, int nblk, int total_blocks, float c2, float rw_mul, int zero_q, int unit) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int N = H * W;
-  const int tid = threadIdx.x;
+  // In the fused call's unit loop: opaque to the compiler, so that the
+  // lane-derived addresses below are recomputed per unit rather than kept
+  // live across the whole loop (which would spill).
+  int tid = static_cast<int>(threadIdx.x);
+  if constexpr (FUSED) __asm__ volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int blk = wave >> 1, par = wave & 1;
 
   // ---- this workgroup's blocks and heads -------------------------------------
-  const int unit = xcd_work_index(static_cast<int>(gridDim.x));
   const int gb0 = unit * kBlocks12;
   const int gb_last = gb0 + kBlocks12 - 1 < total_blocks - 1 ? gb0 + kBlocks12 - 1 : total_blocks - 1;
   const int bhA = gb0 / nblk;
@@ -130,6 +216,25 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   const int q0 = (gb - bh * nblk) * 32;
   const int hs = bh - bhA;  // head slot of this wave's block
   const size_t head = static_cast<size_t>(bh) * N;
+
+  // ---- the fused call: this block's bias rows into the workgroup's slot ---------
+  // The even wave of the block writes rel_h, the odd one rel_w, each staging
+  // through its own 13 KB of LDS (free until pair 0 is staged below).
+  const float* rh_rows = rel_h + (head + q0) * H;
+  const float* rw_rows = rel_w + (head + q0) * W;
+  if constexpr (FUSED) {
+    float* brow = ws + (static_cast<size_t>(blockIdx.x) * kBlocks12 + blk) * 32 * (H + W);
+    if (bvalid) {
+      fused_bias_rows<BF16>(q + (head + q0) * kD, th, tw, brow, par, q0 / W, q0 % W, H, W,
+                            reinterpret_cast<float*>(smem) + wave * 32 * 104, lane);
+    }
+    // the rows are read back by this wave only (through the same L1)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    rh_rows = brow;
+    rw_rows = brow + 32 * H;
+  }
 
   const int band_tiles = (H + kTileRows - 1) / kTileRows;
   const int T = band_tiles * ((W + kTileCols - 1) / kTileCols);
@@ -254,8 +359,8 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   // key column, reloaded per 16-column band), rel_h and the reference maximum
   // in one fma per score (as in the 32-query kernel).
   const int rows = N - q0 < 32 ? N - q0 : 32;
-  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rel_w + (head + q0) * W, static_cast<uint32_t>(rows * W) * 4);
-  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rel_h + (head + q0) * H, static_cast<uint32_t>(rows * H) * 4);
+  const __amdgpu_buffer_rsrc_t rwrs = make_rsrc(rw_rows, static_cast<uint32_t>(rows * W) * 4);
+  const __amdgpu_buffer_rsrc_t rhrs = make_rsrc(rh_rows, static_cast<uint32_t>(rows * H) * 4);
   const int qrow = qok ? ql : 0;
   const int rw_lane = (qrow * W + 4 * half) * 4;
   const int rh_lane = qrow * H * 4;
@@ -592,9 +697,46 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB>
+// Unit `it`-th of this workgroup in a persistent grid over `units` units:
+// XCD x (workgroups with blockIdx % 8 == x) takes a contiguous range of units,
+// its workgroups every n_x-th of them; `units` when there is none left.
+__device__ __forceinline__ int persistent_unit(int it, int units) {
+  const int P = static_cast<int>(gridDim.x);
+  const int x = static_cast<int>(blockIdx.x) & 7;
+  const int per = units >> 3, rem = units & 7;
+  const int start = x * per + (x < rem ? x : rem);
+  const int cnt = per + (x < rem ? 1 : 0);
+  const int nx = (P >> 3) + ((P & 7) > x ? 1 : 0);
+  const int li = (static_cast<int>(blockIdx.x) >> 3) + it * nx;
+  return li < cnt ? start + li : units;
+}
+
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB, bool FUSED>
+__global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
+    const float* __restrict__ rel_w, void* __restrict__ out,
+    const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw, float* __restrict__ ws,
+    int H, int W, int nblk, int total_blocks, int units, float c2, float rw_mul, int zero_q) {
+  if constexpr (FUSED) {
+    // one workgroup per compute unit, each with its own bias slot, over all units
+    for (int it = 0;; ++it) {
+      const int unit = persistent_unit(it, units);
+      if (unit >= units) break;
+      attn12_unit<BF16, OUT_F32, ALIGNED, PB, true>(q, k, v, rel_h, rel_w, out, th, tw, ws, H, W, nblk,
+                                                    total_blocks, c2, rw_mul, zero_q, unit);
+      __syncthreads();  // the next unit reuses the LDS and the slot
+    }
+  } else {
+    attn12_unit<BF16, OUT_F32, ALIGNED, PB, false>(q, k, v, rel_h, rel_w, out, th, tw, ws, H, W, nblk,
+                                                   total_blocks, c2, rw_mul, zero_q,
+                                                   xcd_work_index(static_cast<int>(gridDim.x)));
+  }
+}
+
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB, bool FUSED>
 hipError_t launch12(const AttnArgs& a, hipStream_t stream) {
-  auto kern = attn12_kernel<BF16, OUT_F32, ALIGNED, PB>;
+  auto kern = attn12_kernel<BF16, OUT_F32, ALIGNED, PB, FUSED>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds12);
   if (err != hipSuccess) return err;
@@ -605,17 +747,20 @@ hipError_t launch12(const AttnArgs& a, hipStream_t stream) {
   const bool zero_q = a.scale == 0.0f;
   const float c2 = zero_q ? kLog2e : a.scale * kLog2e;
   const float rw_mul = zero_q ? 1.0f : kLog2e / c2;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(units)), dim3(kThreads12), kLds12, stream,
+  const int grid = FUSED ? (units < a.split_ctas ? units : a.split_ctas) : units;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads12), kLds12, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out, a.H, a.W, nblk, total, c2,
-                     rw_mul, zero_q ? 1 : 0);
+                     static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
+                     static_cast<const uint16_t*>(a.th), static_cast<const uint16_t*>(a.tw),
+                     static_cast<float*>(a.ws), a.H, a.W, nblk, total, units, c2, rw_mul, zero_q ? 1 : 0);
   return hipGetLastError();
 }
 
 template <bool BF16, bool OUT_F32, bool PB>
 hipError_t launch12_al(const AttnArgs& a, hipStream_t stream) {
   const bool aligned = a.H % kTileRows == 0 && a.W % kTileCols == 0;
-  return aligned ? launch12<BF16, OUT_F32, true, PB>(a, stream) : launch12<BF16, OUT_F32, false, PB>(a, stream);
+  return aligned ? launch12<BF16, OUT_F32, true, PB, false>(a, stream)
+                 : launch12<BF16, OUT_F32, false, PB, false>(a, stream);
 }
 
 }  // namespace
@@ -636,6 +781,28 @@ hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream) {
     return a.out_f32 ? launch12_al<true, true, false>(a, stream) : launch12_al<true, false, false>(a, stream);
   }
   return a.out_f32 ? launch12_al<false, true, false>(a, stream) : launch12_al<false, false, false>(a, stream);
+}
+
+}  // namespace relpos
+
+namespace relpos {
+
+bool attn_fused12_ok(int H, int W, bool bf16) {
+  // whole-row blocks (each block of 32 queries inside one grid row), whole
+  // 4 x 16 key tiles, bf16 P
+  return bf16 && W % 32 == 0 && H % 4 == 0 && attn12_fits(H, W) && attn12_bf16_p(H, W);
+}
+
+size_t attn_fused12_workspace_bytes(int64_t BH, int H, int W, int ctas) {
+  const int64_t units = (BH * ((static_cast<int64_t>(H) * W + 31) / 32) + kBlocks12 - 1) / kBlocks12;
+  const int64_t slots = units < ctas ? units : ctas;
+  return static_cast<size_t>(slots) * kBlocks12 * 32 * (H + W) * 4;
+}
+
+hipError_t launch_attn_fused12(const AttnArgs& a, hipStream_t stream) {
+  // H % 4 == 0 and W % 32 == 0 (attn_fused12_ok): the aligned tile path
+  return a.out_f32 ? launch12<true, true, true, true, true>(a, stream)
+                   : launch12<true, false, true, true, true>(a, stream);
 }
 
 }  // namespace relpos

@@ -119,6 +119,13 @@ bool attn12_fits(int H, int W);
 // Whether the kernel runs P.V in bf16 for bf16 inputs on this grid.
 bool attn12_bf16_p(int H, int W);
 hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream);
+// The fused call on the 12-wave kernel: a persistent grid of min(units,
+// split_ctas) workgroups, each computing its blocks' bias rows into its slot
+// of ws (kBlocks12 * 32 * (H + W) floats) before the key loop.  For bf16
+// inputs with W % 32 == 0, H % 4 == 0 and the kernel's bf16-P grids.
+bool attn_fused12_ok(int H, int W, bool bf16);
+size_t attn_fused12_workspace_bytes(int64_t BH, int H, int W, int ctas);
+hipError_t launch_attn_fused12(const AttnArgs& a, hipStream_t stream);
 
 // The 16-query-per-wave kernel (relpos_attn16.hip).
 size_t attn16_lds_bytes();

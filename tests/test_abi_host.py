@@ -356,10 +356,21 @@ def _fused_ws(lib, B, heads, H, W, dt, cus=256):
 
 
 def test_fused_workspace_bytes(lib):
+    # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 1024): one slot
+    # of 6 blocks x 32 queries x (H + W) floats per workgroup of a persistent
+    # grid of min(units, CUs) workgroups, units = ceil(B*heads*N/32 / 6).
+    # 64x64, 12 heads: 256 units on 256 CUs -> exactly the rel_h/rel_w size.
+    assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 256 * 192 * 128 * 4 == 12 * 4096 * 128 * 4
+    # 96x96, 2x16 heads: 1536 units on 256 CUs -> 256 slots
+    assert _fused_ws(lib, 2, 16, 96, 96, BF16) == 256 * 192 * 192 * 4
+    # one 64x64 head: 22 units -> 22 slots
+    assert _fused_ws(lib, 1, 1, 64, 64, BF16) == 22 * 192 * 128 * 4
+    # Otherwise the split-grid kernel: two split pieces and one slot of bias
+    # rows (256 queries) per CU.
     piece = 2 * (256 * 64 + 2 * 256)
-    # 64x64: rows padded to 64 + 64 floats per query, 256 queries per slot
-    assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 256 * (piece + 256 * 128) * 4
-    # 48x80 -> 48 + 80; 7x9 -> 8 + 16; 1x1 -> 4 + 16
+    # 64x64 fp16: rows padded to 64 + 64 floats per query, 256 queries per slot
+    assert _fused_ws(lib, 1, 12, 64, 64, FP16) == 256 * (piece + 256 * 128) * 4
+    # 48x80 (W % 32 != 0) -> 48 + 80; 7x9 -> 8 + 16; 1x1 -> 4 + 16
     assert _fused_ws(lib, 2, 12, 48, 80, BF16, cus=128) == 128 * (piece + 256 * 128) * 4
     assert _fused_ws(lib, 1, 1, 7, 9, FP16, cus=8) == 8 * (piece + 256 * 24) * 4
     assert _fused_ws(lib, 1, 1, 1, 1, BF16, cus=1) == (piece + 256 * 20) * 4
@@ -419,14 +430,17 @@ def _scratch_bytes():
 
 
 def test_scratch_size_covers_the_workloads(lib):
-    # 96 MiB holds relpos_attn_fused's workspace on 256 CUs whenever
-    # roundup(H, 4) + roundup(W, 16) <= 252: the 64x64, 48x80 and 96x96 grids.
+    # 96 MiB holds relpos_attn_fused's workspace on 256 CUs for every batch
+    # size of the workloads here: the 12-wave kernel's when H + W <= 512, the
+    # split-grid kernel's when roundup(H, 4) + roundup(W, 16) <= 252.
     cap = _scratch_bytes()
     assert cap == 96 << 20
-    for H, W in ((64, 64), (48, 80), (96, 96), (14, 14), (92, 160)):
-        assert _fused_ws(lib, 1, 1, H, W, BF16) <= cap, (H, W)
-    for H, W in ((128, 128), (92, 176)):
-        assert _fused_ws(lib, 1, 1, H, W, BF16) > cap, (H, W)
+    for B, heads, H, W, dt in ((1, 12, 64, 64, BF16), (64, 12, 64, 64, BF16), (4, 12, 64, 64, FP16),
+                               (2, 12, 48, 80, BF16), (64, 16, 96, 96, BF16), (25, 12, 14, 14, BF16),
+                               (1, 1, 92, 160, BF16), (64, 1, 256, 256, BF16)):
+        assert _fused_ws(lib, B, heads, H, W, dt) <= cap, (B, heads, H, W)
+    for B, heads, H, W, dt in ((1, 16, 256, 288, BF16), (1, 1, 92, 176, BF16), (1, 1, 128, 128, FP16)):
+        assert _fused_ws(lib, B, heads, H, W, dt) > cap, (B, heads, H, W)
 
 
 def test_noalloc_argument_errors(lib):

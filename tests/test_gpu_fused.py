@@ -31,8 +31,13 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _ws_bytes(H, W):
-    """The size include/relpos.h documents for relpos_attn_fused."""
+def _ws_bytes(H, W, BH=2, dtype="bf16"):
+    """The size include/relpos.h documents for relpos_attn_fused: the 12-wave
+    kernel's slots where it runs (bf16, W % 32 == 0, H % 4 == 0, N >= 1024),
+    else the split-grid kernel's pieces and bias slots."""
+    if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 1024:
+        units = (BH * ((H * W + 31) // 32) + 5) // 6
+        return min(units, _cus()) * 6 * 32 * (H + W) * 4
     rows = (H + 3) // 4 * 4 + (W + 15) // 16 * 16
     return _cus() * (2 * (256 * 64 + 2 * 256) + 256 * rows) * 4
 
@@ -52,8 +57,47 @@ def _filled_ws(H, W, byte):
 
 
 def test_workspace_size_matches_header():
-    for H, W in ((64, 64), (48, 80), (7, 9), (1, 1)):
+    for H, W in ((64, 64), (48, 80), (7, 9), (1, 1), (32, 32), (96, 96)):
         assert rp.fused_workspace_bytes(1, 2, H, W, torch.bfloat16, _cus()) == _ws_bytes(H, W)
+        assert rp.fused_workspace_bytes(1, 2, H, W, torch.float16, _cus()) == _ws_bytes(H, W, dtype="fp16")
+    assert rp.fused_workspace_bytes(4, 12, 64, 64, torch.bfloat16, _cus()) == _ws_bytes(64, 64, BH=48)
+
+
+# ---- the 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 1024) -------------
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(B=1, heads=1, H=32, W=32)),    # 6 units, the last with 2 of 6 blocks
+    ("tiny", dict(B=1, heads=3, H=32, W=64)),    # 64 blocks per head: units span two heads
+    ("tiny", dict(B=2, heads=30, H=32, W=32)),   # 320 units: workgroups take two units in turn
+    ("rect", dict(B=1, heads=2, H=36, W=96)),    # 36 rows: a column band of 9 tiles
+])
+def test_twelve_wave_fused_full(name, kw):
+    d = G.make(name, **kw)
+    assert rp.fused_workspace_bytes(d["q"].shape[0], d["q"].shape[1], d["H"], d["W"], d["q"].dtype, _cus()) == \
+        _ws_bytes(d["H"], d["W"], BH=d["q"].shape[0] * d["q"].shape[1])
+    print(f"[fused] 12-wave {name} {kw}", flush=True)
+    ref, _, _ = G.oracle_full(d)
+    out = _fused(d, _filled_ws(d["H"], d["W"], 0x7f) if d["q"].shape[0] * d["q"].shape[1] <= 2 else None)
+    _check(f"12-wave {name} {kw}", np.abs(G.f64(out) - ref))
+    two, _, _ = G.gpu_run(d)
+    assert (out - two).abs().max().item() <= G.MAX_ABS
+    assert torch.equal(out, _fused(d)), "run-to-run difference"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_twelve_wave_fused_scale(scale):
+    d = G.make("tiny", B=1, heads=2, H=32, W=64)
+    d["scale"] = scale
+    ref, _, _ = G.oracle_full(d)
+    _check(f"12-wave scale {scale}", np.abs(G.f64(_fused(d)) - ref))
+
+
+def test_twelve_wave_fused_half_output():
+    d = G.make("tiny", B=1, heads=2, H=32, W=32)
+    out = _fused(d, out_dtype=torch.bfloat16)
+    ref, _, _ = G.oracle_full(d)
+    err = np.abs(G.f64(out) - ref)
+    assert (err <= G.MAX_ABS + 2.0 ** -8 * np.abs(ref)).all()
 
 
 def test_tiny_full():
@@ -142,7 +186,7 @@ def test_no_allocation_during_calls():
     g = G.to_dev(d)
     H, W = d["H"], d["W"]
     out = torch.empty(g["q"].shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(_ws_bytes(H, W), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(_ws_bytes(H, W, BH=12), dtype=torch.uint8, device="cuda")
     call = lambda: rp.relpos_attn_fused(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], H, W,
                                         d["scale"], out=out, workspace=ws)
     call()
