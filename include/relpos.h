@@ -122,7 +122,7 @@ relpos_status relpos_build(const void* q, const void* rel_pos_h, const void* rel
  *   out_dtype  RELPOS_FP32, or equal to in_dtype
  *   stream     hipStream_t to enqueue on
  * Precision of P.V (fp32 accumulation throughout): for bf16 inputs on grids
- * of N >= 1024 keys where configuration 6 runs (relpos_attn_config), P is
+ * of N >= 2048 keys where configuration 6 runs (relpos_attn_config), P is
  * rounded to bf16 and v used as is; otherwise P is rounded to fp16 and bf16 v
  * is converted to fp16 when staged.  Rounding P to bf16 adds an error that
  * averages over the keys (mean |error| 3.5e-5 at 64x64, 2.3e-5 at 96x96 on
@@ -197,7 +197,7 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  * Defines the same `out` as relpos_build + relpos_attn_fwd on the same inputs
  * (same tolerance against the definition; results differ from the two-call
  * path by rounding only).  Two launch forms, chosen by the grid:
- *   - bf16 inputs with W % 32 == 0, H % 4 == 0, H*W >= 1024 and at least 6
+ *   - bf16 inputs with W % 32 == 0, H % 4 == 0, H*W >= 2048 and at least 6
  *     blocks of 32 queries per (b, h): the 12-wave kernel of configuration 6
  *     on a persistent grid of min(units, CUs) workgroups (units =
  *     ceil(B*heads*H*W/32 / 6)).  For each unit a workgroup first computes its
@@ -300,7 +300,7 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
  *      compute unit; the two waves of a block take the even and the odd key
  *      tiles and merge at the end, and a workgroup may cover the last blocks
  *      of one (b, h) and the first of the next.  Needs N >= 192 and the full
- *      160 KB LDS.  Considered for bf16 inputs with N >= 1024 (where its P.V
+ *      160 KB LDS.  Considered for bf16 inputs with N >= 2048 (where its P.V
  *      runs in bf16), at 0.75 * 1.05 of a configuration-0 round per round of
  *      ceil(B*heads*ceil(N/32)/6) workgroups.
  *

@@ -18,7 +18,7 @@
 //     per head it spans, all by LDS-direct 16-byte buffer loads that pass no
 //     data through registers: 8 waves load V, 4 load K, at the top of step t
 //     into the slot step t+1 reads (two LDS slots).  P.V runs on bf16 MFMA
-//     with P rounded to bf16 for bf16 inputs on grids of >= 1024 keys, so V is
+//     with P rounded to bf16 for bf16 inputs on grids of >= 2048 keys, so V is
 //     staged as loaded; fp16 inputs likewise in fp16.  Otherwise (bf16, fewer
 //     keys) P is fp16, and bf16 V lands in a raw area first and each V wave
 //     converts its own 16 bytes per lane to fp16 at the end of the step.
@@ -60,9 +60,9 @@ static_assert(kOutBase12 + kWaves12 * 32 * kOutStride12 * 4 <= kLds12, "output s
 // bf16 (8 significant bits) adds to each output an error that averages out
 // over the keys; emulated in float64 on the workloads here, its mean over
 // the outputs is 3.4e-5 at N = 4096 and 2.3e-5 at N = 9216 (1.2e-4 at N =
-// 256), against a 1e-4 bar, and it falls as 1/sqrt(N).  Smaller grids keep
-// fp16 P.
-constexpr int kBf16PMinKeys = 1024;
+// 256; measured 6.8e-5 at N = 1024), against a 1e-4 bar, and it falls as
+// 1/sqrt(N).  Smaller grids keep fp16 P.
+constexpr int kBf16PMinKeys = 2048;
 
 // Byte offset of K chunk c (16 bytes, d = 8c .. 8c+7) of tile row o: rows of
 // 128 bytes, chunk index XOR-ed with bits 1..3 of the row, so that the 16

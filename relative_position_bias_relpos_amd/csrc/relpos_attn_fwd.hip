@@ -636,12 +636,12 @@ __device__ __forceinline__ void attn_segment(
   const int slot_last = (T - 1) & (kSlots - 1);
   step(0, True{}, sA, sB, pB, pA);
   int t = 1;
-  if constexpr (!SPLIT || ALIGNED) {
+  if constexpr (!SPLIT || (ALIGNED && !FUSED)) {
     // Unrolled by four: with t = 1 (mod 4) at each iteration every LDS slot
     // of the four steps is a compile-time offset (no per-step address
     // arithmetic; 64x64: 74.3 -> 71.2 us).  The persistent kernels on ragged
-    // grids keep the two-step loop: unrolled by four they spill registers in
-    // the key loop (the tile-aligned fused kernel spills two outside it).
+    // grids and the fused kernels keep the two-step loop: unrolled by four
+    // they spill registers (in the key loop, resp. 2-4 outside it).
     for (; t + 3 < T; t += 4) {
       step(t, False{}, sB, sA, pA, pB);
       step(t + 1, False{}, sA, sB, pB, pA);

@@ -193,7 +193,7 @@ TWELVE = 6
 
 
 def test_attn_config_on_the_workloads(lib):
-    # bf16 with N >= 1024: the 12-wave kernel (192 queries per workgroup, a
+    # bf16 with N >= 2048: the 12-wave kernel (192 queries per workgroup, a
     # round at 0.91 * 0.75 * 1.05 = 0.717).
     # 64x64, 12 heads: 1536 blocks of 32 = 256 workgroups, one round (0.717),
     # against 192 8-wave workgroups in one round (0.91).
@@ -215,11 +215,13 @@ def test_attn_config_on_the_workloads(lib):
 
 
 def test_attn_config_twelve_wave_limits(lib):
-    # bf16 below 1024 keys (fp16 P there) is left to the other kernels:
-    # 16x32 grids, 96 heads = 3072 blocks of 32 would be 512 workgroups.
+    # bf16 below 2048 keys (fp16 P there) is left to the other kernels:
+    # 16x32 grids, 96 heads = 3072 blocks of 32 would be 512 workgroups;
+    # 32x32 grids, 12 heads.
     assert _cfg(lib, 1, 96, 16, 32, BF16) != TWELVE
-    # From 1024 keys on: 16x64, 12 heads, 64 workgroups in one round.
-    assert _cfg(lib, 1, 12, 16, 64, BF16) == TWELVE
+    assert _cfg(lib, 1, 12, 32, 32, BF16) != TWELVE
+    # From 2048 keys on: 32x64, 12 heads, 128 workgroups in one round.
+    assert _cfg(lib, 1, 12, 32, 64, BF16) == TWELVE
     # More than one round where 8-wave units fill the chip evenly: 64x64 with
     # 16 heads is exactly 256 8-wave workgroups (0.91) against 342 12-wave
     # workgroups (two rounds, 1.43).
@@ -356,7 +358,7 @@ def _fused_ws(lib, B, heads, H, W, dt, cus=256):
 
 
 def test_fused_workspace_bytes(lib):
-    # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 1024): one slot
+    # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 2048): one slot
     # of 6 blocks x 32 queries x (H + W) floats per workgroup of a persistent
     # grid of min(units, CUs) workgroups, units = ceil(B*heads*N/32 / 6).
     # 64x64, 12 heads: 256 units on 256 CUs -> exactly the rel_h/rel_w size.

@@ -33,9 +33,9 @@ def _cus():
 
 def _ws_bytes(H, W, BH=2, dtype="bf16"):
     """The size include/relpos.h documents for relpos_attn_fused: the 12-wave
-    kernel's slots where it runs (bf16, W % 32 == 0, H % 4 == 0, N >= 1024),
+    kernel's slots where it runs (bf16, W % 32 == 0, H % 4 == 0, N >= 2048),
     else the split-grid kernel's pieces and bias slots."""
-    if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 1024:
+    if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 2048:
         units = (BH * ((H * W + 31) // 32) + 5) // 6
         return min(units, _cus()) * 6 * 32 * (H + W) * 4
     rows = (H + 3) // 4 * 4 + (W + 15) // 16 * 16
@@ -63,12 +63,12 @@ def test_workspace_size_matches_header():
     assert rp.fused_workspace_bytes(4, 12, 64, 64, torch.bfloat16, _cus()) == _ws_bytes(64, 64, BH=48)
 
 
-# ---- the 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 1024) -------------
+# ---- the 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 2048) -------------
 
 @pytest.mark.parametrize("name,kw", [
-    ("tiny", dict(B=1, heads=1, H=32, W=32)),    # 6 units, the last with 2 of 6 blocks
+    ("tiny", dict(B=1, heads=1, H=32, W=64)),    # 11 units, the last with 4 of 6 blocks
     ("tiny", dict(B=1, heads=3, H=32, W=64)),    # 64 blocks per head: units span two heads
-    ("tiny", dict(B=2, heads=30, H=32, W=32)),   # 320 units: workgroups take two units in turn
+    ("tiny", dict(B=2, heads=15, H=32, W=64)),   # 320 units: workgroups take two units in turn
     ("rect", dict(B=1, heads=2, H=36, W=96)),    # 36 rows: a column band of 9 tiles
 ])
 def test_twelve_wave_fused_full(name, kw):
@@ -93,7 +93,7 @@ def test_twelve_wave_fused_scale(scale):
 
 
 def test_twelve_wave_fused_half_output():
-    d = G.make("tiny", B=1, heads=2, H=32, W=32)
+    d = G.make("tiny", B=1, heads=2, H=32, W=64)
     out = _fused(d, out_dtype=torch.bfloat16)
     ref, _, _ = G.oracle_full(d)
     err = np.abs(G.f64(out) - ref)
