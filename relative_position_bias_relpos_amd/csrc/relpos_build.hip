@@ -29,6 +29,17 @@
 // just read them in the attention call, the rows took 15.4-17.5 us at 64x64
 // with 12 heads (right after that call) against 9.6 us now.  Grids of more
 // than 2^26 units fall back to x = units of one (b, h), y = B*heads.
+//
+// Small grids (H, W <= 32, e.g. windows of 14x14) take a second kernel: there
+// a unit of the kernel above covers one grid row of W < 32 queries and a
+// 64-column MFMA product of which it uses H or W columns, and its rows of H
+// or W floats are too short for 16-byte stores.  Instead a unit is 32
+// consecutive queries of one (b, h) in token order; both tables have at most
+// 63 rows, so the unit forms the full products Gh = Q T_h^T and Gw = Q T_w^T
+// (2 x 32 columns each), stages them in LDS and writes its rel_h and rel_w
+// rows, which are contiguous in memory, as one run of 16-byte pieces each:
+// element f of the run is row m = f / H (f / W), column c of query i = i0 + m,
+// taken from Gh[m, qh - c + H - 1] (Gw[m, qw - c + W - 1]).
 #include "relpos_attn_common.hpp"
 #include "relpos_device.hpp"
 #include "relpos_kernels.hpp"
@@ -182,9 +193,116 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// x / d for 0 <= x < 2048 and 1 <= d <= 32, with m = ceil(2^16 / d): the
+// error of x*m / 2^16 against x/d is below x/2^16 < 1/32 <= 1/d.
+__device__ __forceinline__ int div_small(int x, uint32_t m) { return static_cast<int>((static_cast<uint32_t>(x) * m) >> 16); }
+
+template <bool BF16>
+__global__ __launch_bounds__(64) void build_small_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ th,
+                                                         const uint16_t* __restrict__ tw,
+                                                         float* __restrict__ rel_h,
+                                                         float* __restrict__ rel_w, int H, int W, int upb,
+                                                         uint32_t mh, uint32_t mw) {
+  __shared__ __attribute__((aligned(16))) float gh[32 * kHStride];
+  __shared__ __attribute__((aligned(16))) float gw[32 * kHStride];
+  const int lane = threadIdx.x;
+  const int ml = lane & 31, half = lane >> 5;
+  // units in (b*heads, 32-query block) order, XCD-matched like the kernel above
+  const int unit = attn::xcd_work_index(static_cast<int>(gridDim.x));
+  const int bhi = unit / upb;
+  const int i0 = (unit - bhi * upb) * 32;
+  const int N = H * W;
+  const int rows = N - i0 < 32 ? N - i0 : 32;
+  const size_t row0 = static_cast<size_t>(bhi) * N + i0;
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row0 * kD, static_cast<uint32_t>(rows) * kD * 2);
+  const __amdgpu_buffer_rsrc_t rth = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+  const __amdgpu_buffer_rsrc_t rtw = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+  const int dchunk = 16 * half;
+  u32x4 a[4], bh[2][4], bw[2][4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml < rows ? ml * kD * 2 + 32 * kd + dchunk : kOob);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int j = 32 * nt + ml;  // table row
+    const int oh = j < 2 * H - 1 ? j * kD * 2 + dchunk : kOob;
+    const int ow = j < 2 * W - 1 ? j * kD * 2 + dchunk : kOob;
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      bh[nt][kd] = buf_load16(rth, oh, 32 * kd);
+      bw[nt][kd] = buf_load16(rtw, ow, 32 * kd);
+    }
+  }
+  auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    f32x16 ch{}, cw{};
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      ch = mfma32<BF16>(a[kd], bh[nt][kd], ch);
+      cw = mfma32<BF16>(a[kd], bw[nt][kd], cw);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      gh[out_row(r) * kHStride + 32 * nt + ml] = ch[r];
+      gw[out_row(r) * kHStride + 32 * nt + ml] = cw[r];
+    }
+  }
+  __syncthreads();
+
+  // One run per table: rows*L floats from element (row0 * L) on; 16-byte
+  // stores where the run starts 16-byte aligned, else one store per float.
+  auto emit = [&](float* __restrict__ dst, const float* g, int L, uint32_t mL, bool is_h) {
+    const int total = rows * L;
+    const bool al = ((row0 * static_cast<size_t>(L)) & 3) == 0;
+    float* run = dst + row0 * L;
+    for (int f0 = 4 * lane; f0 < total; f0 += 256) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = f0 + e < total ? f0 + e : total - 1;
+        const int m = div_small(f, mL);
+        const int c = f - m * L;
+        const int i = i0 + m;
+        const int qr = div_small(i, mw);  // grid row of query i
+        const int a_ = is_h ? qr : i - qr * W;
+        v[e] = g[m * kHStride + a_ - c + L - 1];
+      }
+      if (al && f0 + 3 < total) {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(run + f0));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (f0 + e < total) run[f0 + e] = v[e];
+        }
+      }
+    }
+  };
+  emit(rel_h, gh, H, mh, true);
+  emit(rel_w, gw, W, mw, false);
+}
+
 }  // namespace
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
+  const int64_t upb = (static_cast<int64_t>(a.H) * a.W + 31) / 32;
+  if (a.H <= 32 && a.W <= 32 && upb * a.BH <= INT32_MAX) {
+    const uint32_t mh = (65536u + a.H - 1) / a.H, mw = (65536u + a.W - 1) / a.W;
+    const dim3 grid(static_cast<unsigned>(upb * a.BH));
+    if (a.bf16) {
+      hipLaunchKernelGGL(build_small_kernel<true>, grid, dim3(64), 0, stream,
+                         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.rel_pos_h),
+                         static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W,
+                         static_cast<int>(upb), mh, mw);
+    } else {
+      hipLaunchKernelGGL(build_small_kernel<false>, grid, dim3(64), 0, stream,
+                         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.rel_pos_h),
+                         static_cast<const uint16_t*>(a.rel_pos_w), a.rel_h, a.rel_w, a.H, a.W,
+                         static_cast<int>(upb), mh, mw);
+    }
+    return hipGetLastError();
+  }
   const int mtn = (a.W + 31) / 32;
   // 1-D (XCD-matched) up to 2^26 workgroups; beyond that x = units of one
   // (b, h), y = B*heads.
