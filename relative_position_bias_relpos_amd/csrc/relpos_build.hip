@@ -76,8 +76,12 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ tw,
                                                    float* __restrict__ rel_h,
                                                    float* __restrict__ rel_w, int H, int W, int mtn) {
-  __shared__ __attribute__((aligned(16))) float stage_h[32 * kHStride];
-  __shared__ __attribute__((aligned(16))) float stage_g[32 * kGStride];
+  // One staging area for both products (the rel_h pass ends with a barrier
+  // before the rel_w pass writes): 13 KB, so that 12 one-wave workgroups fit
+  // a CU's LDS, as many as its registers allow.
+  __shared__ __attribute__((aligned(16))) float stage[32 * kGStride];
+  float* const stage_h = stage;
+  float* const stage_g = stage;
   const int lane = threadIdx.x;
   const int ml = lane & 31, half = lane >> 5;
   // Units in (b*heads, grid row, 32-query chunk) order.  On the 1-D grid the
