@@ -36,6 +36,22 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def roofline(flops, nbytes, ms, traffic):
+    """The attention call against the roof that bounds it: MFMA when its
+    arithmetic intensity (FLOP per algorithmic byte) is above the ridge
+    PEAK_TFLOPS / PEAK_HBM_GBS (about 313 FLOP/B), else HBM."""
+    intensity = flops / nbytes
+    common = {"kernel": "relpos_attn_fwd", "traffic": traffic, "algorithmic_bytes": nbytes,
+              "flop_per_byte": round(intensity, 1)}
+    if intensity >= PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS, 4), **common}
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), **common}
+
+
 def load_traffic(workload):
     """HBM bytes per attention launch from committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
@@ -447,16 +463,7 @@ def main():
         "rocm": rocm_version(),
         "torch_hip": torch.version.hip,
         "host_us_per_attn_call": {"python_binding": round(host_us, 2), "c_call_only": round(c_us, 2)},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "relpos_attn_fwd",
-            "achieved": round(attn_tflops, 2),
-            "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": attn_bytes,
-        },
+        "roofline": roofline(flops, attn_bytes, attn_ms, traffic),
         "fused": {
             "call": "relpos_attn_fused (bias rows computed in the attention kernel; no rel_h/rel_w tensors)",
             "ms_per_call": round(fused_ms, 5),
