@@ -126,13 +126,22 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
   if (axis == 0) {
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
     for (int n0 = 0; n0 < H; n0 += 64) {
+      // every table fragment of the chunk in flight at once (raw buffer loads,
+      // zeros past the table), then the MFMAs
+      u32x4 b[2][4];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int kh = n0 + 32 * nt + ml;
         const int off = kh < H ? (qh - kh + H - 1) * kD * 2 + dchunk : kOob;
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) b[nt][kd] = buf_load16(rt, off, 32 * kd);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
         f32x16 acc{};
 #pragma unroll
-        for (int kd = 0; kd < 4; ++kd) acc = mfma32<BF16>(a[kd], buf_load16(rt, off, 32 * kd), acc);
+        for (int kd = 0; kd < 4; ++kd) acc = mfma32<BF16>(a[kd], b[nt][kd], acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) stage[out_row(r) * kHS + 32 * nt + ml] = acc[r];
       }
@@ -153,13 +162,20 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
     for (int n0 = 0; n0 < W; n0 += 64) {
       const int tlo = m0 - n0 - 63 + W - 1;
+      u32x4 b[3][4];
 #pragma unroll
       for (int gt = 0; gt < 3; ++gt) {
         const int t = tlo + 32 * gt + ml;
         const int off = t >= 0 && t <= 2 * W - 2 ? t * kD * 2 + dchunk : kOob;
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) b[gt][kd] = buf_load16(rt, off, 32 * kd);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+#pragma unroll
+      for (int gt = 0; gt < 3; ++gt) {
         f32x16 g{};
 #pragma unroll
-        for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], buf_load16(rt, off, 32 * kd), g);
+        for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], b[gt][kd], g);
 #pragma unroll
         for (int r = 0; r < 16; ++r) stage[out_row(r) * kGS + 32 * gt + ml] = g[r];
       }
