@@ -196,7 +196,14 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  *
  * Defines the same `out` as relpos_build + relpos_attn_fwd on the same inputs
  * (same tolerance against the definition; results differ from the two-call
- * path by rounding only).  Two launch forms, chosen by the grid:
+ * path by rounding only).  Three launch forms, chosen by the grid:
+ *   - H <= 32, W <= 32 and at most four key tiles of 4 grid rows x 16
+ *     columns (ceil(H/4) * ceil(W/16) <= 4; the 14 x 14 windows of windowed
+ *     attention, 16 x 16, 8 x 32): the 16-query kernel of configuration 3,
+ *     whose workgroup of 64 queries first forms their bias rows on MFMA
+ *     (fp32 accumulation) into LDS, 64*(H + W) floats beside the K/V
+ *     staging, and reads them from there in the key loop.  No workspace: the
+ *     workspace argument is not read and may be NULL with workspace_bytes 0.
  *   - bf16 inputs with W % 32 == 0, H % 4 == 0, H*W >= 2048 and at least 6
  *     blocks of 32 queries per (b, h): the 12-wave kernel of configuration 6
  *     on a persistent grid of min(units, CUs) workgroups (units =
@@ -221,15 +228,17 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  *   rel_pos_w  [2W-1, D]  in_dtype (device)
  *   workspace  device scratch, 16-byte aligned, not overlapping any other
  *              operand; contents on entry are not read.  Calls sharing a
- *              workspace must not run concurrently.
+ *              workspace must not run concurrently.  Not read, and not
+ *              checked, on the small grids of the first form.
  *   workspace_bytes  >= relpos_fused_workspace_bytes(...) for the current
  *              device (else E_SHAPE); negative is E_VALUE.
  * Errors: E_SHAPE, E_DTYPE, E_VALUE, E_NULL, E_ALIGN, E_ALIAS (out or the
  * workspace overlapping another operand), E_DEVICE, E_HIP (device query),
  * E_LAUNCH.  Check order: sizes, dtypes, scalars; then (B*heads > 0) NULL and
- * alignment of all seven pointers, out overlapping an input; then the
- * device's compute-unit count is queried, and the workspace size (E_SHAPE),
- * workspace overlap and device memory of every operand are checked.
+ * alignment of all seven pointers (six on the small grids of the first
+ * form), out overlapping an input; then the device's compute-unit count is
+ * queried, and the workspace size (E_SHAPE), workspace overlap and device
+ * memory of every operand are checked.
  */
 relpos_status relpos_attn_fused(const void* q, const void* k, const void* v,
                                 const void* rel_pos_h, const void* rel_pos_w, void* out,
@@ -270,8 +279,9 @@ relpos_status relpos_attn_fused_noalloc(const void* q, const void* k, const void
 
 /*
  * relpos_fused_workspace_bytes: workspace bytes relpos_attn_fused needs on a
- * device with `cu_count` compute units.  With the 12-wave kernel (the first
- * form above): min(units, cu_count) * 6 * 32 * (H + W) * 4, one slot of bias
+ * device with `cu_count` compute units.  0 on the small grids of the first
+ * form above (H, W <= 32, ceil(H/4) * ceil(W/16) <= 4).  With the 12-wave
+ * kernel (the second form): min(units, cu_count) * 6 * 32 * (H + W) * 4, one slot of bias
  * rows per workgroup -- at most the size of the rel_h / rel_w tensors it
  * replaces once B*heads*H*W/192 >= cu_count (25.2 MB at 64x64 with 12 heads).
  * Otherwise:

@@ -274,8 +274,9 @@ def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_
     q, k, v and the tables, without rel_h/rel_w tensors.
 
     workspace: "auto" (default) uses a scratch workspace cached per (device,
-    stream) until release_workspaces(); a uint8 device tensor of at least
-    fused_workspace_bytes() is used as given.
+    stream) until release_workspaces(), or none where fused_workspace_bytes()
+    is 0 (grids of at most 32 x 32 with at most four key tiles); a uint8
+    device tensor of at least fused_workspace_bytes() is used as given.
     """
     lib = _load()
     B, nh, D, out = _fused_operands(q, k, v, rel_pos_h, rel_pos_w, H, W, out, out_dtype)
@@ -283,12 +284,13 @@ def relpos_attn_fused(q, k, v, rel_pos_h, rel_pos_w, H, W, scale, out=None, out_
         if workspace != "auto":
             raise ValueError('workspace must be "auto" or a tensor')
         need = fused_workspace_bytes(B, nh, H, W, q.dtype, _cu_count(q.device))
-        workspace = _cached_workspace(q.device, _stream(q).value, need)
-    if not isinstance(workspace, torch.Tensor):
+        workspace = _cached_workspace(q.device, _stream(q).value, need) if need > 0 else None
+    elif not isinstance(workspace, torch.Tensor):
         raise TypeError('workspace must be "auto" or a tensor')
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.relpos_attn_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_pos_h), _ptr(rel_pos_w), _ptr(out),
                                B, nh, H, W, D, float(scale), _DT[q.dtype], _DT[out.dtype],
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+                               _ptr(workspace), ws_bytes, _stream(q))
     _check("relpos_attn_fused", st)
     return out
 

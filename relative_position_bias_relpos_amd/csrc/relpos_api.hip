@@ -391,6 +391,7 @@ int64_t relpos_fused_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_
                                      int cu_count) {
   int64_t BH = 0;
   if (check_dims(B, heads, H, W, 64, &BH) != RELPOS_OK || !is_half(in_dtype) || cu_count < 1) return -1;
+  if (relpos::attn_fused16_ok(static_cast<int>(H), static_cast<int>(W))) return 0;
   if (relpos::attn_fused12_ok(static_cast<int>(H), static_cast<int>(W), in_dtype == RELPOS_BF16)) {
     return static_cast<int64_t>(
         relpos::attn_fused12_workspace_bytes(BH, static_cast<int>(H), static_cast<int>(W), cu_count));
@@ -448,8 +449,15 @@ relpos_status fused_impl(const void* q, const void* k, const void* v, const void
       {out, out_bytes},
       {workspace, 0},
   };
-  // The scratch array is not the caller's: only the six operands are checked.
-  const int nops = from_scratch ? 6 : 7;
+  // Three launch forms: the 16-query kernel with the bias rows in LDS (small
+  // grids, no workspace), the 12-wave fused kernel where the grid allows it,
+  // else the split-grid one.
+  const bool f16 = relpos::attn_fused16_ok(static_cast<int>(H), static_cast<int>(W));
+  const bool f12 =
+      !f16 && relpos::attn_fused12_ok(static_cast<int>(H), static_cast<int>(W), in_dtype == RELPOS_BF16);
+  // The scratch array is not the caller's, and the 16-query form takes no
+  // workspace: then only the six operands are checked.
+  const int nops = from_scratch || f16 ? 6 : 7;
   if ((st = check_align(ops, nops)) != RELPOS_OK) return st;
   for (int i = 0; i < 5; ++i) {
     if (overlaps(ops[5], ops[i])) return RELPOS_E_ALIAS;
@@ -457,8 +465,20 @@ relpos_status fused_impl(const void* q, const void* k, const void* v, const void
   // The workspace size depends on the device's compute-unit count.
   DeviceProps props{};
   if (device_props(&props) != 0) return RELPOS_E_HIP;
-  // The 12-wave fused kernel where the grid allows it, else the split-grid one.
-  const bool f12 = relpos::attn_fused12_ok(static_cast<int>(H), static_cast<int>(W), in_dtype == RELPOS_BF16);
+  if (f16) {
+    if (relpos::attn_fused16_lds_bytes(static_cast<int>(H), static_cast<int>(W)) >
+        static_cast<size_t>(props.lds_limit)) {
+      return RELPOS_E_SHAPE;
+    }
+    if ((st = check_device(ops, 6)) != RELPOS_OK) return st;
+    relpos::AttnArgs a{q, k, v, nullptr, nullptr, out,
+                       static_cast<int>(BH), static_cast<int>(H), static_cast<int>(W), scale,
+                       in_dtype == RELPOS_BF16, out_dtype == RELPOS_FP32};
+    a.th = rel_pos_h;
+    a.tw = rel_pos_w;
+    if (relpos::launch_attn_fused16(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RELPOS_E_LAUNCH;
+    return RELPOS_OK;
+  }
   const size_t need = f12 ? relpos::attn_fused12_workspace_bytes(BH, static_cast<int>(H), static_cast<int>(W), props.cus)
                           : relpos::attn_fused_workspace_bytes(static_cast<int>(H), static_cast<int>(W), props.cus);
   if (from_scratch) {

@@ -23,6 +23,13 @@
 //   * Online softmax with a lazy reference maximum, as in the 32-query kernel:
 //     m moves only on the first tile or when a tile's rounded-p sum exceeds
 //     2^15; the row sum adds the rounded fp16 p.
+//   * FUSED (relpos_attn_fused on grids with H, W <= 32 and at most four key
+//     tiles, e.g. windows of 14x14): the workgroup first computes the rel_h
+//     and rel_w rows of its 64 queries into LDS, with relpos_build's
+//     small-grid products (both tables have at most 63 rows, so 32 queries'
+//     products Q T^T are two 32x32 MFMA tiles per table; waves 0/2 take rel_h,
+//     1/3 rel_w, of queries 0-31 / 32-63), and reads its bias from there: no
+//     workspace and no rel_h / rel_w tensors.
 #include <type_traits>
 
 #include "relpos_attn_common.hpp"
@@ -38,13 +45,69 @@ constexpr int kKSlots16 = 2;
 constexpr int kVSlots16 = 3;
 
 constexpr int NW = 4;
+constexpr int kGStride16 = 72;  // floats per staged product row (64 used)
 
-template <bool BF16, bool OUT_F32>
+// x / d for 0 <= x < 2048 and 1 <= d <= 32, with m = ceil(2^16 / d): the
+// error of x*m / 2^16 against x/d is below x/2^16 < 1/32 <= 1/d.
+__device__ __forceinline__ int div_small16(int x, uint32_t m) {
+  return static_cast<int>((static_cast<uint32_t>(x) * m) >> 16);
+}
+
+// Bias rows of `rows` (<= 32) consecutive queries i0 .. of one (b, h) into LDS
+// (H, W <= 32): axis 0 writes rel_h [rows][H], axis 1 rel_w [rows][W] at dst,
+// row-major.  G = Q T^T over all 2L-1 table rows (2 MFMA tiles), staged in
+// `stage` (this wave's 32 x 72 floats), then element (m, c) of the rows is
+// G[m, a - c + L - 1] with a the query's grid row (axis 0) or column.  The
+// same products and order as relpos_build's small-grid kernel.
+template <bool BF16>
+__device__ __forceinline__ void bias_rows_lds(const uint16_t* __restrict__ qrows, int rows,
+                                              const uint16_t* __restrict__ tab, int axis, int i0, int H, int W,
+                                              uint32_t mh, uint32_t mw, float* stage, float* dst, int lane) {
+  const int ml = lane & 31, half = lane >> 5;
+  const int L = axis == 0 ? H : W;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qrows, static_cast<uint32_t>(rows) * kD * 2);
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(tab, static_cast<uint32_t>(2 * L - 1) * kD * 2);
+  const int dchunk = 16 * half;
+  u32x4 a[4], b[2][4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml < rows ? ml * kD * 2 + 32 * kd + dchunk : kOob);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int j = 32 * nt + ml;
+    const int off = j < 2 * L - 1 ? j * kD * 2 + dchunk : kOob;
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) b[nt][kd] = buf_load16(rt, off, 32 * kd);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    f32x16 g{};
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], b[nt][kd], g);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) stage[(8 * (r >> 2) + 4 * half + (r & 3)) * kGStride16 + 32 * nt + ml] = g[r];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t mL = axis == 0 ? mh : mw;
+  const int total = rows * L;
+  for (int f = lane; f < total; f += 64) {
+    const int m = div_small16(f, mL);
+    const int c = f - m * L;
+    const int i = i0 + m;
+    const int qr = div_small16(i, mw);  // grid row of query i
+    const int av = axis == 0 ? qr : i - qr * W;
+    dst[f] = stage[m * kGStride16 + av - c + L - 1];
+  }
+}
+
+template <bool BF16, bool OUT_F32, bool FUSED>
 __global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
     const float* __restrict__ rel_w, void* __restrict__ out,
-    int H, int W, int q_tiles, float c2) {
+    const uint16_t* __restrict__ th, const uint16_t* __restrict__ tw,
+    int H, int W, int q_tiles, float c2, uint32_t mh, uint32_t mw) {
   constexpr int BM = 16 * NW;
   constexpr int NT = NW * 64;
   const int N = H * W;
@@ -63,6 +126,24 @@ __global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
   const int bh = work / q_tiles;
   const int q0 = (work - bh * q_tiles) * BM;
   const size_t head = static_cast<size_t>(bh) * N;
+
+  // ---- FUSED: the bias rows of the workgroup's 64 queries into LDS ------------
+  // (rel_h [64][H] then rel_w [64][W] after the K/V ring; the products are
+  // staged in the ring's space, which the tiles take only after the barrier)
+  float* const bias_h = reinterpret_cast<float*>(smem + (kKSlots16 + kVSlots16) * kTileHalves * 2);
+  float* const bias_w = bias_h + BM * H;
+  if constexpr (FUSED) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int jb = wv >> 1, axis = wv & 1;
+    const int i0 = q0 + 32 * jb;
+    const int rows = N - i0 < 32 ? N - i0 : 32;
+    if (rows > 0) {
+      bias_rows_lds<BF16>(q + (head + i0) * kD, rows, axis == 0 ? th : tw, axis, i0, H, W, mh, mw,
+                          reinterpret_cast<float*>(smem) + wv * 32 * kGStride16,
+                          axis == 0 ? bias_h + 32 * jb * H : bias_w + 32 * jb * W, lane);
+    }
+    __syncthreads();
+  }
 
   // ---- Q^T operand fragments: d = 32*kd + 8*grp .. +7 ------------------------
   const int qrow = wave * 16 + col;
@@ -125,17 +206,25 @@ __global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
   // byte range and the offsets stay far inside 32 bits for every grid).
   const int unit_rows = N - q0 < BM ? N - q0 : BM;
   const __amdgpu_buffer_rsrc_t rwrs =
-      make_rsrc(rel_w + (head + q0) * W, static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(W) * 4);
+      make_rsrc(FUSED ? nullptr : rel_w + (head + q0) * W,
+                static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(W) * 4);
   const __amdgpu_buffer_rsrc_t rhrs =
-      make_rsrc(rel_h + (head + q0) * H, static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(H) * 4);
-  const int rw_off = (qi < N ? qrow : 0) * W * 4;
-  const int rh_off = (qi < N ? qrow : 0) * H * 4;
+      make_rsrc(FUSED ? nullptr : rel_h + (head + q0) * H,
+                static_cast<uint32_t>(unit_rows) * static_cast<uint32_t>(H) * 4);
+  const int brow = qi < N ? qrow : 0;  // queries past the grid read row 0's bias
+  const int rw_off = brow * W * 4;
+  const int rh_off = brow * H * 4;
   float rw[4];
   auto load_band = [&](int kw0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = kw0 + 4 * grp + j;
-      const float x = buf_loadf(rwrs, c < W ? rw_off + 4 * c : kOob);
+      float x;
+      if constexpr (FUSED) {
+        x = c < W ? bias_w[brow * W + c] : 0.f;
+      } else {
+        x = buf_loadf(rwrs, c < W ? rw_off + 4 * c : kOob);
+      }
       rw[j] = (c < W) ? x * kLog2e : -__builtin_inff();
     }
   };
@@ -143,7 +232,12 @@ __global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
   auto load_rh = [&](int kh0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x = buf_loadf(rhrs, kh0 + r < H ? rh_off + 4 * (kh0 + r) : kOob);
+      float x;
+      if constexpr (FUSED) {
+        x = kh0 + r < H ? bias_h[brow * H + kh0 + r] : 0.f;
+      } else {
+        x = buf_loadf(rhrs, kh0 + r < H ? rh_off + 4 * (kh0 + r) : kOob);
+      }
       rhn[r] = (kh0 + r < H) ? x * kLog2e : -__builtin_inff();
     }
   };
@@ -322,20 +416,22 @@ __global__ __launch_bounds__(NW * 64, 3) void attn16_kernel(
   }
 }
 
-template <bool BF16, bool OUT_F32>
+template <bool BF16, bool OUT_F32, bool FUSED>
 hipError_t launch16(const AttnArgs& a, hipStream_t stream) {
-  auto kern = attn16_kernel<BF16, OUT_F32>;
-  const size_t lds = attn16_lds_bytes();
+  auto kern = attn16_kernel<BF16, OUT_F32, FUSED>;
+  const size_t lds = FUSED ? attn_fused16_lds_bytes(a.H, a.W) : attn16_lds_bytes();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
   constexpr int BM = 16 * NW;
   const int q_tiles = (a.H * a.W + BM - 1) / BM;
   dim3 grid(static_cast<unsigned>(q_tiles * a.BH));
+  const uint32_t mh = (65536u + a.H - 1) / a.H, mw = (65536u + a.W - 1) / a.W;
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.rel_h, a.rel_w, a.out,
-                     a.H, a.W, q_tiles, a.scale * kLog2e);
+                     static_cast<const uint16_t*>(a.th), static_cast<const uint16_t*>(a.tw),
+                     a.H, a.W, q_tiles, a.scale * kLog2e, mh, mw);
   return hipGetLastError();
 }
 
@@ -343,11 +439,27 @@ hipError_t launch16(const AttnArgs& a, hipStream_t stream) {
 
 size_t attn16_lds_bytes() { return static_cast<size_t>(kKSlots16 + kVSlots16) * kTileHalves * 2; }
 
+size_t attn_fused16_lds_bytes(int H, int W) {
+  return attn16_lds_bytes() + static_cast<size_t>(16 * NW) * (H + W) * 4;
+}
+
+bool attn_fused16_ok(int H, int W) {
+  const int T = ((H + kTileRows - 1) / kTileRows) * ((W + kTileCols - 1) / kTileCols);
+  return H <= 32 && W <= 32 && T <= 4;
+}
+
 hipError_t launch_attn16(const AttnArgs& a, hipStream_t stream) {
   if (a.bf16) {
-    return a.out_f32 ? launch16<true, true>(a, stream) : launch16<true, false>(a, stream);
+    return a.out_f32 ? launch16<true, true, false>(a, stream) : launch16<true, false, false>(a, stream);
   }
-  return a.out_f32 ? launch16<false, true>(a, stream) : launch16<false, false>(a, stream);
+  return a.out_f32 ? launch16<false, true, false>(a, stream) : launch16<false, false, false>(a, stream);
+}
+
+hipError_t launch_attn_fused16(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) {
+    return a.out_f32 ? launch16<true, true, true>(a, stream) : launch16<true, false, true>(a, stream);
+  }
+  return a.out_f32 ? launch16<false, true, true>(a, stream) : launch16<false, false, true>(a, stream);
 }
 
 }  // namespace relpos

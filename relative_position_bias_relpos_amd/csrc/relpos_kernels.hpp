@@ -130,5 +130,11 @@ hipError_t launch_attn_fused12(const AttnArgs& a, hipStream_t stream);
 // The 16-query-per-wave kernel (relpos_attn16.hip).
 size_t attn16_lds_bytes();
 hipError_t launch_attn16(const AttnArgs& a, hipStream_t stream);
+// The fused call on the 16-query kernel, for grids with H, W <= 32 and at
+// most 4 key tiles: each workgroup computes its 64 queries' bias rows into
+// LDS (attn_fused16_lds_bytes) from the tables th / tw; no workspace.
+bool attn_fused16_ok(int H, int W);
+size_t attn_fused16_lds_bytes(int H, int W);
+hipError_t launch_attn_fused16(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace relpos

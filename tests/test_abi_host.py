@@ -372,10 +372,19 @@ def test_fused_workspace_bytes(lib):
     piece = 2 * (256 * 64 + 2 * 256)
     # 64x64 fp16: rows padded to 64 + 64 floats per query, 256 queries per slot
     assert _fused_ws(lib, 1, 12, 64, 64, FP16) == 256 * (piece + 256 * 128) * 4
-    # 48x80 (W % 32 != 0) -> 48 + 80; 7x9 -> 8 + 16; 1x1 -> 4 + 16
+    # 48x80 (W % 32 != 0) -> 48 + 80; 4x48 -> 4 + 48; 20x16 -> 20 + 16
     assert _fused_ws(lib, 2, 12, 48, 80, BF16, cus=128) == 128 * (piece + 256 * 128) * 4
-    assert _fused_ws(lib, 1, 1, 7, 9, FP16, cus=8) == 8 * (piece + 256 * 24) * 4
-    assert _fused_ws(lib, 1, 1, 1, 1, BF16, cus=1) == (piece + 256 * 20) * 4
+    assert _fused_ws(lib, 1, 1, 4, 48, FP16, cus=8) == 8 * (piece + 256 * 52) * 4
+    assert _fused_ws(lib, 1, 1, 20, 16, BF16, cus=1) == (piece + 256 * 36) * 4
+    # H, W <= 32 with at most 4 key tiles (4x16 each): the 16-query kernel with
+    # the bias rows in LDS, no workspace (14x14 windows, 16x16, 7x9, 8x32, 1x1)
+    for H, W in ((14, 14), (16, 16), (7, 9), (8, 32), (1, 1), (4, 32), (16, 8)):
+        assert _fused_ws(lib, 25, 12, H, W, BF16) == 0, (H, W)
+        assert _fused_ws(lib, 1, 1, H, W, FP16, cus=1) == 0, (H, W)
+    # more key tiles, or a side above 32: a workspace
+    assert _fused_ws(lib, 1, 1, 17, 16, BF16) > 0   # 5 tiles
+    assert _fused_ws(lib, 1, 1, 12, 32, BF16) > 0   # 6 tiles
+    assert _fused_ws(lib, 1, 1, 4, 33, BF16) > 0    # W > 32
     assert _fused_ws(lib, 1, 1, 8, 8, FP32) == -1
     assert _fused_ws(lib, 1, 1, 0, 8, BF16) == -1
     assert _fused_ws(lib, 1, 1, 8, 8, BF16, cus=0) == -1
@@ -398,20 +407,40 @@ def test_fused_is_declared_with_its_workspace_query():
 
 
 def test_fused_pointer_errors(lib):
+    # 20 x 16 (five key tiles) takes a workspace: all seven pointers are checked.
     base = P + [0x10000 * 7]
     for i in range(7):
         p = list(base)
         p[i] = None
-        assert _fused(lib, ptrs=p) == E_NULL, i
+        assert _fused(lib, ptrs=p, H=20, W=16) == E_NULL, i
         p = list(base)
         p[i] += 4
-        assert _fused(lib, ptrs=p) == E_ALIGN, i
-    p = list(base)
-    p[5] = p[0]  # out == q
-    assert _fused(lib, ptrs=p) == E_ALIAS
-    p = list(base)
-    p[5] = p[3]  # out over rel_pos_h
-    assert _fused(lib, ptrs=p) == E_ALIAS
+        assert _fused(lib, ptrs=p, H=20, W=16) == E_ALIGN, i
+    for H, W in ((20, 16), (4, 4)):
+        p = list(base)
+        p[5] = p[0]  # out == q
+        assert _fused(lib, ptrs=p, H=H, W=W) == E_ALIAS
+        p = list(base)
+        p[5] = p[3]  # out over rel_pos_h
+        assert _fused(lib, ptrs=p, H=H, W=W) == E_ALIAS
+
+
+def test_fused_small_grid_ignores_workspace(lib):
+    # H, W <= 32 with at most four key tiles: the bias rows live in LDS and the
+    # workspace argument is not read, so a NULL or unaligned one passes the
+    # pointer checks (the call then stops at the planted out == q overlap).
+    base = P + [0x10000 * 7]
+    for H, W in ((4, 4), (14, 14), (16, 16), (1, 1), (16, 8)):
+        for ws in (None, base[6] + 4):
+            p = list(base)
+            p[6] = ws
+            p[5] = p[0]
+            assert _fused(lib, ptrs=p, H=H, W=W, ws_bytes=0) == E_ALIAS, (H, W, ws)
+        for i in range(6):
+            p = list(base)
+            p[6] = None
+            p[i] = None
+            assert _fused(lib, ptrs=p, H=H, W=W, ws_bytes=0) == E_NULL, (H, W, i)
 
 
 # ---- relpos_attn_fused_noalloc (host-side checks) ----------------------------------

@@ -31,10 +31,19 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+def _small_grid(H, W):
+    """Grids whose bias rows the 16-query kernel forms in LDS: H, W <= 32 and
+    at most four key tiles of 4 grid rows x 16 columns."""
+    return H <= 32 and W <= 32 and ((H + 3) // 4) * ((W + 15) // 16) <= 4
+
+
 def _ws_bytes(H, W, BH=2, dtype="bf16"):
-    """The size include/relpos.h documents for relpos_attn_fused: the 12-wave
-    kernel's slots where it runs (bf16, W % 32 == 0, H % 4 == 0, N >= 2048),
-    else the split-grid kernel's pieces and bias slots."""
+    """The size include/relpos.h documents for relpos_attn_fused: none on small
+    grids, the 12-wave kernel's slots where it runs (bf16, W % 32 == 0,
+    H % 4 == 0, N >= 2048), else the split-grid kernel's pieces and bias
+    slots."""
+    if _small_grid(H, W):
+        return 0
     if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 2048:
         units = (BH * ((H * W + 31) // 32) + 5) // 6
         return min(units, _cus()) * 6 * 32 * (H + W) * 4
@@ -57,7 +66,7 @@ def _filled_ws(H, W, byte):
 
 
 def test_workspace_size_matches_header():
-    for H, W in ((64, 64), (48, 80), (7, 9), (1, 1), (32, 32), (96, 96)):
+    for H, W in ((64, 64), (48, 80), (7, 9), (1, 1), (32, 32), (96, 96), (14, 14), (16, 16), (20, 12), (4, 48)):
         assert rp.fused_workspace_bytes(1, 2, H, W, torch.bfloat16, _cus()) == _ws_bytes(H, W)
         assert rp.fused_workspace_bytes(1, 2, H, W, torch.float16, _cus()) == _ws_bytes(H, W, dtype="fp16")
     assert rp.fused_workspace_bytes(4, 12, 64, 64, torch.bfloat16, _cus()) == _ws_bytes(64, 64, BH=48)
@@ -207,14 +216,17 @@ def test_no_allocation_during_calls():
 def test_last_round_with_one_idle_cu():
     """units = CUs - 1: splitting would put every tail on the one idle CU, so
     the fused launch keeps the last round whole.  Parity, and a time of the
-    order of one unit's work (not one tail per unit in a row)."""
+    order of one unit's work (not one tail per unit in a row).  20 x 12 has
+    five key tiles, so it takes the split-grid form."""
     cus = _cus()
-    d = G.make("tiny", B=1, heads=cus - 1, H=16, W=16)
+    H, W = 20, 12
+    assert not _small_grid(H, W)
+    d = G.make("tiny", B=1, heads=cus - 1, H=H, W=W)
     ref, _, _ = G.oracle_full(d)
     _check(f"{cus - 1} units", np.abs(G.f64(_fused(d)) - ref))
     g = G.to_dev(d)
-    ws = torch.empty(_ws_bytes(16, 16), dtype=torch.uint8, device="cuda")
-    call = lambda: rp.relpos_attn_fused(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], 16, 16,
+    ws = torch.empty(_ws_bytes(H, W), dtype=torch.uint8, device="cuda")
+    call = lambda: rp.relpos_attn_fused(g["q"], g["k"], g["v"], g["rel_pos_h"], g["rel_pos_w"], H, W,
                                         d["scale"], workspace=ws)
     call()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -225,7 +237,7 @@ def test_last_round_with_one_idle_cu():
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / 5
-    print(f"[fused] {cus - 1} units of 4 tiles: {ms * 1e3:.1f} us", flush=True)
+    print(f"[fused] {cus - 1} units of 5 tiles: {ms * 1e3:.1f} us", flush=True)
     assert ms < 1.0
 
 
@@ -238,3 +250,40 @@ def test_rel_h_rows_at_the_lds_limit(H, W):
     _check(f"fused {H}x{W}", np.abs(G.f64(_fused(d)) - ref))
     two, _, _ = G.gpu_run(d)
     _check(f"two calls {H}x{W}", np.abs(G.f64(two) - ref))
+
+
+# ---- small grids: the 16-query kernel with its bias rows in LDS (no workspace) ----
+
+SMALL = [(1, 1), (1, 7), (5, 3), (7, 9), (14, 14), (16, 16), (16, 8), (4, 32), (8, 32), (2, 17), (13, 11),
+         (16, 1), (8, 31)]
+
+
+@pytest.mark.parametrize("H,W", SMALL)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_small_grid_fused_full(H, W, dtype):
+    """Every output against the oracle; no workspace is passed, and the
+    result equals the two-call path's within the bar and does not change
+    when a (filled) workspace is given, which the call does not read."""
+    assert _small_grid(H, W) and _ws_bytes(H, W) == 0
+    d = G.make("tiny", seed=H * 53 + W, B=2, heads=3, H=H, W=W, dtype=dtype)
+    print(f"[fused] small grid {H}x{W} {dtype}", flush=True)
+    ref, _, _ = G.oracle_full(d)
+    out = _fused(d)
+    _check(f"small {H}x{W} {dtype}", np.abs(G.f64(out) - ref))
+    two, _, _ = G.gpu_run(d)
+    assert (out - two).abs().max().item() <= G.MAX_ABS
+    ws = torch.full((4096,), 0xff, dtype=torch.uint8, device="cuda")
+    assert torch.equal(out, _fused(d, ws))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_small_grid_fused_half_output(dtype):
+    d = G.make("tiny", dtype=dtype, B=2, heads=2, H=14, W=14)
+    out = _fused(d, out_dtype=d["q"].dtype)
+    assert out.dtype == d["q"].dtype
+    ref, _, _ = G.oracle_full(d)
+    err = np.abs(G.f64(out) - ref)
+    ulp = 2.0 ** (-8 if dtype == "bf16" else -11)
+    assert (err <= G.MAX_ABS + ulp * np.abs(ref)).all(), dtype
+    print(f"[fused] small 14x14 out={dtype}: max={err.max():.3e} mean={err.mean():.3e}", flush=True)
+

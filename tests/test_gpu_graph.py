@@ -89,7 +89,8 @@ def test_graph_replays_match_eager(name, kw):
     assert not torch.equal(got, ref), name
 
 
-@pytest.mark.parametrize("name,kw", [("rect", dict(B=1, heads=3, H=21, W=35)), ("deepencoder", {})])
+@pytest.mark.parametrize("name,kw", [("rect", dict(B=1, heads=3, H=21, W=35)), ("deepencoder", {}),
+                                     ("tiny", dict(B=2, heads=3, H=14, W=14))])
 def test_fused_graph_replays_match_eager(name, kw):
     """relpos_attn_fused with a caller workspace under capture: the persistent
     kernel and the merge replay to the eager result and follow input updates."""
