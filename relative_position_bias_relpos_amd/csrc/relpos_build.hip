@@ -52,20 +52,32 @@ constexpr int kD = 64;
 constexpr int kHStride = 72;   // floats per staged rel_h row (64 used)
 constexpr int kGStride = 104;  // floats per staged G row (95 used)
 
+// Cache policy of the row stores of build_kernel: sc1 (device scope: written
+// through to memory, so the kernel ends with no dirty L2 lines of rows to
+// write back) and nt (streaming).  Back to back: 9.1-9.2 against 9.6 us at
+// 64x64 with 12 heads, 54.7-55.1 against 56.8 us at 96x96 with 32 heads,
+// 25.5 against 24.5 us for 4 x 12 heads of 64x64 (nt alone: the previous
+// figures; plain stores 10.9-11.3 us at 64x64).  The small-grid kernel keeps
+// plain non-temporal stores (its 14x14 windows: 7.3-7.5 against 8.4-8.6 us
+// written through).
+constexpr int kRowStorePolicy = 16 | 2;
+
 // 16 bytes of output: 4 consecutive floats of one row from column n (a
 // multiple of 4) on, the part below `cols` (a row's length) written; one
-// 16-byte store where the rows keep 16-byte alignment (cols % 4 == 0, the
-// tensors being 16-byte aligned), else one store per float.  Non-temporal:
-// the rows are read by the next kernel, from other XCDs' L2s; at 64x64 this
-// is 9.3 against 10.1 us back to back, and 15.4 against 17.5 us right after
-// an attention call that read the same rel_h / rel_w.
-__device__ __forceinline__ void store_row4(float* dst, int n, int cols, f32x4 v) {
-  if ((cols & 3) == 0 && n < cols) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + n));
+// 16-byte buffer store where the rows keep 16-byte alignment (cols % 4 == 0,
+// the tensors being 16-byte aligned), else one 4-byte store per float.  `rs`
+// covers the unit's rows, `off` is the byte offset of the row in it.
+__device__ __forceinline__ void store_row4(__amdgpu_buffer_rsrc_t rs, int off, int n, int cols, f32x4 v) {
+  if ((cols & 3) == 0) {
+    if (n < cols) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off + 4 * n, 0, kRowStorePolicy);
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (n + e < cols) dst[n + e] = v[e];
+      if (n + e < cols) {
+        __builtin_amdgcn_raw_buffer_store_b32(as_uint(v[e]), rs, off + 4 * (n + e), 0, kRowStorePolicy);
+      }
     }
   }
 }
@@ -109,6 +121,11 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t rth = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
   const __amdgpu_buffer_rsrc_t rtw = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
   const int dchunk = 16 * half;  // byte offset of this lane's 8 d values within a 16-wide slice
+  // the unit's rel_h and rel_w rows (store targets)
+  const __amdgpu_buffer_rsrc_t rsh =
+      make_rsrc(rel_h + row0 * H, static_cast<uint32_t>(rows) * static_cast<uint32_t>(H) * 4);
+  const __amdgpu_buffer_rsrc_t rsw =
+      make_rsrc(rel_w + row0 * W, static_cast<uint32_t>(rows) * static_cast<uint32_t>(W) * 4);
 
   // A operand: query m0 + ml, d = 16*kd + 8*half .. +7
   u32x4 a[4];
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = sr + 4 * i;
-      if (m < rows) store_row4(rel_h + (row0 + m) * H, n0 + sc, H, v[i]);
+      if (m < rows) store_row4(rsh, m * H * 4, n0 + sc, H, v[i]);
     }
     __syncthreads();
   }
@@ -191,7 +208,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = sr + 4 * i;
-      if (m < rows) store_row4(rel_w + (row0 + m) * W, n0 + sc, W, v[i]);
+      if (m < rows) store_row4(rsw, m * W * 4, n0 + sc, W, v[i]);
     }
     __syncthreads();
   }
