@@ -196,13 +196,187 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
   }
 }
 
+// Bias rows kept in LDS (the fused call, single-head units, H <= 64 and W <=
+// 64, bf16 P): a workgroup spanning one head uses one 32 KB pair of each
+// slot and not the raw-V area, which leaves three 32 KB regions free; block
+// b's rel_h rows go to region b/2 at (b%2) * 16 KB, its rel_w rows 8 KB
+// further.  A row is 64 floats (256 B) whose 16-byte chunk c sits at chunk c
+// ^ (row % 16), so that the 32 rows a key-loop read touches at one column
+// cover the 64 banks twice.
+__device__ __forceinline__ int lb_block_off(int b) {
+  return (b < 2 ? kPairBytes12 : b < 4 ? kSlotBytes12 + kPairBytes12 : 2 * kSlotBytes12) + (b & 1) * 16384;
+}
+__device__ __forceinline__ int lb_off(int row, int col) {
+  return row * 256 + 16 * ((col >> 2) ^ (row & 15)) + 4 * (col & 3);
+}
+static_assert(2 * kSlotBytes12 + 32768 <= kLds12, "the third bias region must fit the LDS");
+
+// The tables staged once per workgroup for the LDS-resident bias: T_h and T_w
+// (2L - 1 <= 127 rows of 128 bytes each, zeros past the last row) in the
+// pair area of slot 1, which pair 1's loads first use in step 0; row t's
+// 16-byte chunk c at chunk c ^ (t % 8), so that the 32 rows an MFMA operand
+// read touches at one chunk spread over all banks.
+constexpr int kTabBytes12 = 16384;
+__device__ __forceinline__ int tab_off(int t, int c) { return t * 128 + 16 * (c ^ (t & 7)); }
+
+// The bias rows of one block of 32 queries (m0 .. m0+31 of grid row qh) for
+// the LDS rows above, by one wave on 32x32x16 MFMA, in two phases around a
+// workgroup barrier (the same products, same order, as relpos_build), with
+// the block's Q fragments `a` and the tables staged in LDS (`tabs`).
+//   Phase 1.  axis 0: acc = the product against the reversed window of T_h,
+//     rel_h[m, kh] = q[m] . T_h[qh - kh + H - 1] (kept in registers).
+//     axis 1: G[m, j] = q[m] . T_w[tlo + j] over the 95 table rows tlo = m0 -
+//     63 + W - 1 .. the block reaches, staged in the block's 16 KB region
+//     (rows of 104 floats) and read back along the diagonal, rel_w[m, n] =
+//     G[m, m - n + 63], into wr (lane: rows lane/16 + 4i, columns 4*(lane%16)
+//     .. +3).  Columns past H (W) get values that are never read; table
+//     rows outside [0, 127] are clamped into the staged area for the same
+//     reason.
+//   Phase 2 (after the barrier, once the odd wave of every block has read its
+//     staged G back): the rows are written to their swizzled places.
+struct BiasRegs {
+  f32x16 acc[2];
+  f32x4 wr[8];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void fused_bias_lds_phase1(const u32x4 (&a)[4], const unsigned char* tabs,
+                                                      unsigned char* region, int axis, int qh, int m0, int H,
+                                                      int W, int lane, BiasRegs& br) {
+  constexpr int kGS = 104;  // staging row stride (floats): the two 32-lane halves on disjoint banks
+  const int ml = lane & 31, half = lane >> 5;
+  auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
+  auto clamp_row = [](int t) { return t < 0 ? 0 : (t > 127 ? 127 : t); };
+  if (axis == 0) {
+    u32x4 b[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int t = clamp_row(qh - (32 * nt + ml) + H - 1);
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) b[nt][kd] = *reinterpret_cast<const u32x4*>(tabs + tab_off(t, 2 * kd + half));
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 acc{};
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) acc = mfma32<BF16>(a[kd], b[nt][kd], acc);
+      br.acc[nt] = acc;
+    }
+  } else {
+    const unsigned char* const tw = tabs + kTabBytes12;
+    const int tlo = m0 - 63 + W - 1;
+    u32x4 b[3][4];
+#pragma unroll
+    for (int gt = 0; gt < 3; ++gt) {
+      const int t = clamp_row(tlo + 32 * gt + ml);
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) b[gt][kd] = *reinterpret_cast<const u32x4*>(tw + tab_off(t, 2 * kd + half));
+    }
+    float* const stage = reinterpret_cast<float*>(region);
+#pragma unroll
+    for (int gt = 0; gt < 3; ++gt) {
+      f32x16 g{};
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) g = mfma32<BF16>(a[kd], b[gt][kd], g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage[out_row(r) * kGS + 32 * gt + ml] = g[r];
+    }
+    // read back by this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int sc = 4 * (lane & 15), sr = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      const float* gp = stage + m * kGS + m - sc + 63;  // G[m, m - (sc + e) + 63]
+      br.wr[i] = f32x4{gp[0], gp[-1], gp[-2], gp[-3]};
+    }
+  }
+}
+
+__device__ __forceinline__ void fused_bias_lds_phase2(unsigned char* region, int axis, int lane,
+                                                      const BiasRegs& br) {
+  const int ml = lane & 31, half = lane >> 5;
+  if (axis == 0) {
+    // element (m, kh), m = 8*(r/4) + 4*half + r%4, kh = 32*nt + ml: chunk
+    // (kh/4) ^ (m % 16) of row m, and m % 16 = c_r | 4*half with c_r =
+    // 8*((r/4) % 2) + r%4, so the lane's chunk is ((kh/4) ^ 4*half) ^ c_r.
+    // Columns kh >= H hold zeros (the table loads there read zeros) and lie
+    // inside the 64-float rows; they are never read.
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int kh = 32 * nt + ml;
+      const int xl = (kh >> 2) ^ (4 * half);
+      unsigned char* const base = region + half * 4 * 256 + 4 * (kh & 3);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cr = 8 * ((r >> 2) & 1) + (r & 3);
+        const int mrow = 8 * (r >> 2) + (r & 3);  // m without the 4*half part
+        *reinterpret_cast<float*>(base + mrow * 256 + 16 * (xl ^ cr)) = br.acc[nt][r];
+      }
+    }
+  } else {
+    const int sc = 4 * (lane & 15), sr = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      *reinterpret_cast<f32x4*>(region + 8192 + lb_off(m, sc)) = br.wr[i];
+    }
+  }
+}
+
+// Phase 2 for a unit whose bias rows go to its workspace slot instead (units
+// spanning two heads, or a partial last unit, on grids with H, W <= 64):
+// rel_h [32][H] at dst through `stage` (rows of 72 floats; the phase-1
+// staging of this block, read back before the barrier), rel_w [32][W] at dst
+// + 32 * H from the registers, as 16-byte stores of whole rows.
+__device__ __forceinline__ void fused_bias_slot_phase2(float* __restrict__ dst, float* stage, int axis, int H,
+                                                       int W, int lane, const BiasRegs& br) {
+  constexpr int kHS = 72;
+  const int ml = lane & 31, half = lane >> 5;
+  const int sc = 4 * (lane & 15), sr = lane >> 4;
+  if (axis == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage[(8 * (r >> 2) + 4 * half + (r & 3)) * kHS + 32 * nt + ml] = br.acc[nt][r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stage + m * kHS + sc);
+      if (sc < H) *reinterpret_cast<f32x4*>(dst + m * H + sc) = x;  // H % 4 == 0 here
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = sr + 4 * i;
+      if (sc < W) *reinterpret_cast<f32x4*>(dst + 32 * H + m * W + sc) = br.wr[i];  // W % 32 == 0 here
+    }
+  }
+}
+
+// Phase-1 staging area of block b for fused_bias_slot_phase2's units: free
+// LDS before pair 0 is loaded (slot 0) and outside the staged tables (slot 1's
+// first 32 KB): 13 KB each in [0, 64 KB) and [96, 128 KB).
+__device__ __forceinline__ int s2_stage_off(int b) { return b < 4 ? b * 13312 : 3 * kPairBytes12 + (b - 4) * 13312; }
+static_assert(3 * 13312 + 13312 <= 2 * kPairBytes12 && 3 * kPairBytes12 + 2 * 13312 <= 2 * kSlotBytes12,
+              "staging areas must fit beside the tables");
+
 // One unit (6 blocks of 32 queries) of the 12-wave kernel.
 // PB (bf16 inputs only): P.V runs in bf16 (P rounded to bf16, V staged as
 // loaded); otherwise in fp16 (bf16 V converted to fp16 while staged).
 // FUSED: the bias rows of the unit's blocks are computed first into this
 // workgroup's slot of `ws` (block b: rel_h [32][H] then rel_w [32][W] at
-// b * 32 * (H + W) floats) and read from there instead of rel_h / rel_w.
-template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB, bool FUSED>
+// b * 32 * (H + W) floats) and read from there instead of rel_h / rel_w;
+// with LB (units within one head, H, W <= 64, bf16 P) into LDS instead;
+// with S2 (the other units on such grids) into the slot, formed from the
+// tables staged in LDS.
+template <bool BF16, bool OUT_F32, bool ALIGNED, bool PB, bool FUSED, bool LB = false, bool S2 = false>
 __device__ __forceinline__ void attn12_unit(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ rel_h,
@@ -238,7 +412,14 @@ __device__ __forceinline__ void attn12_unit(
   // through its own 13 KB of LDS (free until pair 0 is staged below).
   const float* rh_rows = rel_h + (head + q0) * H;
   const float* rw_rows = rel_w + (head + q0) * W;
-  if constexpr (FUSED) {
+  static_assert(!LB || (FUSED && PB), "bias rows in LDS only in the fused call with bf16 P");
+  static_assert(!S2 || (FUSED && PB && !LB), "two-phase slot rows only in the fused call with bf16 P");
+  float* const s2_rows = ws + (static_cast<size_t>(blockIdx.x) * kBlocks12 + blk) * 32 * (H + W);
+  if constexpr (S2) {
+    rh_rows = s2_rows;
+    rw_rows = s2_rows + 32 * H;
+  }
+  if constexpr (FUSED && !LB && !S2) {
     float* brow = ws + (static_cast<size_t>(blockIdx.x) * kBlocks12 + blk) * 32 * (H + W);
     if (bvalid) {
       fused_bias_rows<BF16>(q + (head + q0) * kD, th, tw, brow, par, q0 / W, q0 % W, H, W,
@@ -381,9 +562,18 @@ __device__ __forceinline__ void attn12_unit(
   const int rw_lane = (qrow * W + 4 * half) * 4;
   const int rh_lane = qrow * H * 4;
   f32x16 rwc;
+  const unsigned char* const lb_rows = smem + lb_block_off(blk);
   auto load_band = [&](int kw0) {
     float x[8];
-    if constexpr (ALIGNED) {
+    if constexpr (LB) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(lb_rows + 8192 + lb_off(qrow, kw0 + 4 * half));
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(lb_rows + 8192 + lb_off(qrow, kw0 + 4 * half + 8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = as_float(a0[i]) * rw_mul;
+        x[4 + i] = as_float(a1[i]) * rw_mul;
+      }
+    } else if constexpr (ALIGNED) {
       const u32x4 a0 = buf_load16(rwrs, rw_lane, 4 * kw0);
       const u32x4 a1 = buf_load16(rwrs, rw_lane + 32, 4 * kw0);
 #pragma unroll
@@ -405,7 +595,11 @@ __device__ __forceinline__ void attn12_unit(
   };
   float rh[4], rh_next[4];  // rel_h of the step's tile; of the next step's, prefetched
   auto load_rh = [&](int kh0) {
-    if constexpr (ALIGNED) {
+    if constexpr (LB) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(lb_rows + lb_off(qrow, kh0));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rh_next[r] = as_float(a[r]);
+    } else if constexpr (ALIGNED) {
       const u32x4 a = buf_load16(rhrs, rh_lane, 4 * kh0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) rh_next[r] = as_float(a[r]);
@@ -435,23 +629,87 @@ __device__ __forceinline__ void attn12_unit(
     v_rd[dt] = (2 + par) * kTileBytes12 + tr_row * 128 + 8 * ((8 * dt + 4 * (grp & 1) + (jl & 3)) ^ vsw);
 
   // ---- prologue: pair 0 in slot 0 ---------------------------------------------
+  // Tables of the LDS-formed bias: once per workgroup into slot 1's first pair
+  // area (1 KB pieces, 16 per table, spread over the waves).
+  auto stage_tables = [&]() {
+    const sgpr4 trs_h = rsrc_words(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+    const sgpr4 trs_w = rsrc_words(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int piece = wave + 12 * i;
+      if (piece < 32) {
+        const int tr = 8 * (piece & 15) + (lane >> 3);
+        lds_load16(piece < 16 ? trs_h : trs_w, tr * 128 + 16 * ((lane & 7) ^ (tr & 7)), 0,
+                   lds0 + kSlotBytes12 + (piece >> 4) * kTabBytes12 + (piece & 15) * 1024);
+      }
+    }
+  };
+  // The block's Q fragments for the bias products (reloaded when scale == 0
+  // zeroed them).
+  auto bias_q = [&](u32x4 (&qa)[4]) {
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      qa[kd] = zero_q == 0 ? qf[kd] : *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half);
+    }
+  };
+  if constexpr (S2) {
+    // Units spanning two heads (or partial) on grids with H, W <= 64: the
+    // rows are formed as for LB, from LDS, before pair 0 is staged (the
+    // staging areas lie in its slot), and written to the workspace slot.
+    stage_tables();
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    u32x4 qa[4];
+    bias_q(qa);
+    BiasRegs br;
+    float* const stage = reinterpret_cast<float*>(smem + s2_stage_off(blk));
+    if (bvalid) {
+      fused_bias_lds_phase1<BF16>(qa, smem + kSlotBytes12, reinterpret_cast<unsigned char*>(stage), par, q0 / W,
+                                  q0 % W, H, W, lane, br);
+    }
+    __syncthreads();
+    if (bvalid) fused_bias_slot_phase2(s2_rows, stage, par, H, W, lane, br);
+    // the rows are read back by this wave only (through the same L1); the
+    // staging areas are free again before pair 0 lands in slot 0
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
   const TilePos p0{0, 0};
   if (v_wave) {
     v_dma(0, vrs0, p0, 0);
     if (two) v_dma(1, vrs1, p0, kPairBytes12);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    v_convert(0, slot_ptr(0));
-    if (two) v_convert(1, slot_ptr(0) + kPairBytes12);
   } else {
     k_dma(krs0, p0, 0);
     if (two) k_dma(krs1, p0, kPairBytes12);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if constexpr (LB) stage_tables();  // beside pair 0's loads
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (v_wave) {
+    v_convert(0, slot_ptr(0));
+    if (two) v_convert(1, slot_ptr(0) + kPairBytes12);
+  }
+  if constexpr (LB) {
+    // Every block valid and in the one head: the even wave forms rel_h, the
+    // odd one rel_w (staging in the block's region), from the block's Q
+    // fragments (reloaded when scale == 0 zeroed them) and the staged tables;
+    // then both write their rows into the region once every odd wave has read
+    // its staging back.
+    __syncthreads();  // tables and pair 0 in LDS
+    u32x4 qa[4];
+    bias_q(qa);
+    BiasRegs br;
+    unsigned char* const region = smem + lb_block_off(blk);
+    fused_bias_lds_phase1<BF16>(qa, smem + kSlotBytes12, region, par, q0 / W, q0 % W, H, W, lane, br);
+    __syncthreads();
+    fused_bias_lds_phase2(region, par, lane, br);
+    __syncthreads();  // the block's rows of both waves written
   }
   TilePos pc = par ? next_tile(p0, H) : p0;  // this wave's tile of the current step
   int band_kw = pc.kw;
   load_band(pc.kw);
   load_rh(pc.kh);
-  __syncthreads();
+  if constexpr (!LB) __syncthreads();
 
   f32x16 acc[2];
   acc[0] = f32x16{};
@@ -665,7 +923,7 @@ __device__ __forceinline__ void attn12_unit(
   const float* theirs = reinterpret_cast<const float*>(smem + (wave ^ 1) * kMergeStride12);
   // the partner finalises output columns 32*(1-par) .. : it needs acc[1-par]
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[1 - par][r];
+  for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = par ? acc[0][r] : acc[1][r];
   if (half == 0) {
     mine[16 * 64 + ql] = m;
     mine[16 * 64 + 32 + ql] = lt;
@@ -686,7 +944,7 @@ __device__ __forceinline__ void attn12_unit(
   for (int g = 0; g < 4; ++g) {
     f32x4 o4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = acc[par][4 * g + e] * ca + theirs[(4 * g + e) * 64 + lane] * cb;
+    for (int e = 0; e < 4; ++e) o4[e] = (par ? acc[1][4 * g + e] : acc[0][4 * g + e]) * ca + theirs[(4 * g + e) * 64 + lane] * cb;
     *reinterpret_cast<f32x4*>(ostage + ql * kOutStride12 + 8 * g + 4 * half) = o4;
   }
   // the rows are read back by other lanes of this wave only
@@ -736,9 +994,29 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     int H, int W, int nblk, int total_blocks, int units, float c2, float rw_mul, int zero_q) {
   if constexpr (FUSED) {
     // one workgroup per compute unit, each with its own bias slot, over all units
+    // Units inside one head keep their bias rows in LDS where they fit (H, W
+    // <= 64); units spanning two heads stage two heads' K/V per slot and use
+    // the workspace slot (formed from the tables staged in LDS on such grids).
+    const bool lds_fits = PB && H <= 64 && W <= 64;
     for (int it = 0;; ++it) {
       const int unit = persistent_unit(it, units);
       if (unit >= units) break;
+      const int gb0 = unit * kBlocks12;
+      const int gb_last = gb0 + kBlocks12 - 1;
+      if constexpr (PB) {
+        if (lds_fits) {
+          if (gb_last < total_blocks && gb_last / nblk == gb0 / nblk) {
+            attn12_unit<BF16, OUT_F32, ALIGNED, PB, true, true>(q, k, v, rel_h, rel_w, out, th, tw, ws, H, W, nblk,
+                                                                total_blocks, c2, rw_mul, zero_q, unit);
+          } else {
+            attn12_unit<BF16, OUT_F32, ALIGNED, PB, true, false, true>(q, k, v, rel_h, rel_w, out, th, tw, ws, H,
+                                                                       W, nblk, total_blocks, c2, rw_mul, zero_q,
+                                                                       unit);
+          }
+          __syncthreads();  // the next unit reuses the LDS and the slot
+          continue;
+        }
+      }
       attn12_unit<BF16, OUT_F32, ALIGNED, PB, true>(q, k, v, rel_h, rel_w, out, th, tw, ws, H, W, nblk,
                                                     total_blocks, c2, rw_mul, zero_q, unit);
       __syncthreads();  // the next unit reuses the LDS and the slot

@@ -93,9 +93,29 @@ def test_twelve_wave_fused_full(name, kw):
     assert torch.equal(out, _fused(d)), "run-to-run difference"
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=1, heads=2, H=64, W=64),   # 43 units: LDS-resident bias, one unit spanning two heads, a partial last unit
+    dict(B=1, heads=3, H=48, W=64),   # 48 units, none spanning two heads: all bias rows in LDS
+    dict(B=1, heads=2, H=64, W=32),   # rows of 32 columns in the 64-column LDS rows
+    dict(B=3, heads=4, H=40, W=64),   # 160 units on fewer workgroups than units when CUs < 160
+])
+def test_twelve_wave_fused_lds_bias(kw):
+    """Grids with H, W <= 64: units inside one head keep their bias rows in
+    LDS, the others in the workspace slot; every output against the oracle,
+    and bit for bit against the two-call path (same products, same order)."""
+    d = G.make("tiny", **kw)
+    print(f"[fused] LDS bias {kw}", flush=True)
+    ref, _, _ = G.oracle_full(d)
+    out = _fused(d)
+    _check(f"LDS bias {kw}", np.abs(G.f64(out) - ref))
+    two, _, _ = G.gpu_run(d, config=6)  # the same 12-wave kernel in the two-call path
+    assert torch.equal(out, two), "fused call differs from relpos_build + relpos_attn_fwd"
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125])
-def test_twelve_wave_fused_scale(scale):
-    d = G.make("tiny", B=1, heads=2, H=32, W=64)
+@pytest.mark.parametrize("H", [32, 64])
+def test_twelve_wave_fused_scale(scale, H):
+    d = G.make("tiny", B=1, heads=2, H=H, W=64)
     d["scale"] = scale
     ref, _, _ = G.oracle_full(d)
     _check(f"12-wave scale {scale}", np.abs(G.f64(_fused(d)) - ref))
