@@ -203,6 +203,7 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
 // further.  A row is 64 floats (256 B) whose 16-byte chunk c sits at chunk c
 // ^ (row % 16), so that the 32 rows a key-loop read touches at one column
 // cover the 64 banks twice.
+constexpr int kLbMaxSide = 64;  // LDS bias rows are 64 floats
 __device__ __forceinline__ int lb_block_off(int b) {
   return (b < 2 ? kPairBytes12 : b < 4 ? kSlotBytes12 + kPairBytes12 : 2 * kSlotBytes12) + (b & 1) * 16384;
 }
@@ -414,7 +415,11 @@ __device__ __forceinline__ void attn12_unit(
   const float* rw_rows = rel_w + (head + q0) * W;
   static_assert(!LB || (FUSED && PB), "bias rows in LDS only in the fused call with bf16 P");
   static_assert(!S2 || (FUSED && PB && !LB), "two-phase slot rows only in the fused call with bf16 P");
-  float* const s2_rows = ws + (static_cast<size_t>(blockIdx.x) * kBlocks12 + blk) * 32 * (H + W);
+  // S2 units have one slot each: a unit spanning heads bhA and bhA + 1 slot
+  // bhA (each head boundary lies in one unit), a partial last unit inside one
+  // head slot B*heads - 1.
+  const int s2_slot = two ? bhA : total_blocks / nblk - 1;
+  float* const s2_rows = ws + (static_cast<size_t>(s2_slot) * kBlocks12 + blk) * 32 * (H + W);
   if constexpr (S2) {
     rh_rows = s2_rows;
     rw_rows = s2_rows + 32 * H;
@@ -997,7 +1002,7 @@ __global__ __launch_bounds__(kThreads12, 1) void attn12_kernel(
     // Units inside one head keep their bias rows in LDS where they fit (H, W
     // <= 64); units spanning two heads stage two heads' K/V per slot and use
     // the workspace slot (formed from the tables staged in LDS on such grids).
-    const bool lds_fits = PB && H <= 64 && W <= 64;
+    const bool lds_fits = PB && H <= kLbMaxSide && W <= kLbMaxSide;
     for (int it = 0;; ++it) {
       const int unit = persistent_unit(it, units);
       if (unit >= units) break;
@@ -1081,6 +1086,8 @@ hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream) {
 
 namespace relpos {
 
+bool attn_fused12_lds_bias(int H, int W) { return H <= kLbMaxSide && W <= kLbMaxSide; }
+
 bool attn_fused12_ok(int H, int W, bool bf16) {
   // whole-row blocks (each block of 32 queries inside one grid row), whole
   // 4 x 16 key tiles, bf16 P
@@ -1088,6 +1095,9 @@ bool attn_fused12_ok(int H, int W, bool bf16) {
 }
 
 size_t attn_fused12_workspace_bytes(int64_t BH, int H, int W, int ctas) {
+  // H, W <= 64: slots only for the units spanning two heads or partial (one
+  // per b*heads); otherwise one slot per workgroup of the persistent grid.
+  if (attn_fused12_lds_bias(H, W)) return static_cast<size_t>(BH) * kBlocks12 * 32 * (H + W) * 4;
   const int64_t units = (BH * ((static_cast<int64_t>(H) * W + 31) / 32) + kBlocks12 - 1) / kBlocks12;
   const int64_t slots = units < ctas ? units : ctas;
   return static_cast<size_t>(slots) * kBlocks12 * 32 * (H + W) * 4;

@@ -124,6 +124,8 @@ hipError_t launch_attn12(const AttnArgs& a, hipStream_t stream);
 // of ws (kBlocks12 * 32 * (H + W) floats) before the key loop.  For bf16
 // inputs with W % 32 == 0, H % 4 == 0 and the kernel's bf16-P grids.
 bool attn_fused12_ok(int H, int W, bool bf16);
+// Grids whose fused units keep their bias rows in LDS (H, W <= 64).
+bool attn_fused12_lds_bias(int H, int W);
 size_t attn_fused12_workspace_bytes(int64_t BH, int H, int W, int ctas);
 hipError_t launch_attn_fused12(const AttnArgs& a, hipStream_t stream);
 

@@ -358,15 +358,22 @@ def _fused_ws(lib, B, heads, H, W, dt, cus=256):
 
 
 def test_fused_workspace_bytes(lib):
-    # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 2048): one slot
-    # of 6 blocks x 32 queries x (H + W) floats per workgroup of a persistent
-    # grid of min(units, CUs) workgroups, units = ceil(B*heads*N/32 / 6).
-    # 64x64, 12 heads: 256 units on 256 CUs -> exactly the rel_h/rel_w size.
-    assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 256 * 192 * 128 * 4 == 12 * 4096 * 128 * 4
+    # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 2048); a slot
+    # is 6 blocks x 32 queries x (H + W) floats.  H, W <= 64: units inside one
+    # head keep their bias rows in LDS, the others (spanning two heads, or a
+    # partial last unit) use one slot per b*heads, whatever the CU count.
+    assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 12 * 192 * 128 * 4          # 1.2 MB
+    assert _fused_ws(lib, 1, 12, 64, 64, BF16, cus=8) == 12 * 192 * 128 * 4
+    assert _fused_ws(lib, 1, 1, 64, 64, BF16) == 192 * 128 * 4
+    assert _fused_ws(lib, 2, 3, 48, 64, BF16) == 6 * 192 * 112 * 4
+    assert _fused_ws(lib, 1, 2, 64, 32, BF16) == 2 * 192 * 96 * 4
+    # larger sides: one slot per workgroup of the persistent grid of
+    # min(units, CUs) workgroups, units = ceil(B*heads*N/32 / 6).
     # 96x96, 2x16 heads: 1536 units on 256 CUs -> 256 slots
     assert _fused_ws(lib, 2, 16, 96, 96, BF16) == 256 * 192 * 192 * 4
-    # one 64x64 head: 22 units -> 22 slots
-    assert _fused_ws(lib, 1, 1, 64, 64, BF16) == 22 * 192 * 128 * 4
+    # one 96x96 head: 48 units -> 48 slots; 64x128 (W > 64): 43 units of 2 heads
+    assert _fused_ws(lib, 1, 1, 96, 96, BF16) == 48 * 192 * 192 * 4
+    assert _fused_ws(lib, 1, 2, 64, 128, BF16) == 86 * 192 * 192 * 4
     # Otherwise the split-grid kernel: two split pieces and one slot of bias
     # rows (256 queries) per CU.
     piece = 2 * (256 * 64 + 2 * 256)

@@ -40,11 +40,13 @@ def _small_grid(H, W):
 def _ws_bytes(H, W, BH=2, dtype="bf16"):
     """The size include/relpos.h documents for relpos_attn_fused: none on small
     grids, the 12-wave kernel's slots where it runs (bf16, W % 32 == 0,
-    H % 4 == 0, N >= 2048), else the split-grid kernel's pieces and bias
-    slots."""
+    H % 4 == 0, N >= 2048: one per b*heads when H, W <= 64, else one per
+    workgroup), else the split-grid kernel's pieces and bias slots."""
     if _small_grid(H, W):
         return 0
     if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 2048:
+        if H <= 64 and W <= 64:  # slots only for units spanning two heads or partial: one per b*heads
+            return BH * 6 * 32 * (H + W) * 4
         units = (BH * ((H * W + 31) // 32) + 5) // 6
         return min(units, _cus()) * 6 * 32 * (H + W) * 4
     rows = (H + 3) // 4 * 4 + (W + 15) // 16 * 16
