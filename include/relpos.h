@@ -209,9 +209,12 @@ int64_t relpos_attn_workspace_bytes(int64_t B, int64_t heads, int64_t H, int64_t
  *     on a persistent grid of min(units, CUs) workgroups (units =
  *     ceil(B*heads*H*W/32 / 6)).  For each unit a workgroup first computes its
  *     6 blocks' bias rows on MFMA (fp32 accumulation, the same products as
- *     relpos_build, so the result equals the two-call path's bit for bit)
- *     into its slot of the workspace, then runs the key loop reading them
- *     from there.  No second kernel.
+ *     relpos_build, so the result equals the two-call path's bit for bit),
+ *     then runs the key loop reading them back.  With H, W <= 64 the tables
+ *     are staged once per workgroup in LDS, a unit inside one head keeps its
+ *     rows in LDS, and only a unit spanning two heads (or a partial last
+ *     unit) puts them in its workspace slot, one slot per b*heads; on larger
+ *     grids every workgroup uses its own slot.  No second kernel.
  *   - otherwise: each workgroup of the persistent split launch of
  *     relpos_attn_fwd_ws (one 8-wave workgroup per compute unit, merge kernel
  *     when split) computes the bias rows of its 256 queries and reads them
@@ -281,10 +284,12 @@ relpos_status relpos_attn_fused_noalloc(const void* q, const void* k, const void
  * relpos_fused_workspace_bytes: workspace bytes relpos_attn_fused needs on a
  * device with `cu_count` compute units.  0 on the small grids of the first
  * form above (H, W <= 32, ceil(H/4) * ceil(W/16) <= 4).  With the 12-wave
- * kernel (the second form): min(units, cu_count) * 6 * 32 * (H + W) * 4, one slot of bias
- * rows per workgroup -- at most the size of the rel_h / rel_w tensors it
- * replaces once B*heads*H*W/192 >= cu_count (25.2 MB at 64x64 with 12 heads).
- * Otherwise:
+ * kernel (the second form): slots * 6 * 32 * (H + W) * 4 with slots =
+ * min(units, cu_count) (one slot of bias rows per workgroup), or, when H, W
+ * <= 64, min(B*heads, units, cu_count) (only the units spanning two heads or
+ * partial use a slot): 1.2 MB at 64x64 with 12 heads, against 25.2 MB of
+ * rel_h / rel_w; one slot per workgroup is at most the size of rel_h / rel_w
+ * once B*heads*H*W/192 >= cu_count.  Otherwise:
  *   cu_count * (2 * (256*64 + 2*256) + 256 * (roundup(H, 4) + roundup(W, 16))) * 4
  * (two split pieces and one slot of bias rows per workgroup).  -1 if a size
  * or the dtype is out of range or cu_count < 1.  Host-only.

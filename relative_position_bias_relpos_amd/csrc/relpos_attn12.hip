@@ -415,10 +415,12 @@ __device__ __forceinline__ void attn12_unit(
   const float* rw_rows = rel_w + (head + q0) * W;
   static_assert(!LB || (FUSED && PB), "bias rows in LDS only in the fused call with bf16 P");
   static_assert(!S2 || (FUSED && PB && !LB), "two-phase slot rows only in the fused call with bf16 P");
-  // S2 units have one slot each: a unit spanning heads bhA and bhA + 1 slot
-  // bhA (each head boundary lies in one unit), a partial last unit inside one
-  // head slot B*heads - 1.
-  const int s2_slot = two ? bhA : total_blocks / nblk - 1;
+  // S2 units have one slot each, one per b*heads when there are at most as
+  // many as workgroups: a unit spanning heads bhA and bhA + 1 slot bhA (each
+  // head boundary lies in one unit), a partial last unit inside one head
+  // slot B*heads - 1; else the workgroup's own slot.
+  const int n_bh = total_blocks / nblk;
+  const int s2_slot = n_bh <= static_cast<int>(gridDim.x) ? (two ? bhA : n_bh - 1) : static_cast<int>(blockIdx.x);
   float* const s2_rows = ws + (static_cast<size_t>(s2_slot) * kBlocks12 + blk) * 32 * (H + W);
   if constexpr (S2) {
     rh_rows = s2_rows;
@@ -1095,11 +1097,12 @@ bool attn_fused12_ok(int H, int W, bool bf16) {
 }
 
 size_t attn_fused12_workspace_bytes(int64_t BH, int H, int W, int ctas) {
-  // H, W <= 64: slots only for the units spanning two heads or partial (one
-  // per b*heads); otherwise one slot per workgroup of the persistent grid.
-  if (attn_fused12_lds_bias(H, W)) return static_cast<size_t>(BH) * kBlocks12 * 32 * (H + W) * 4;
+  // One slot per workgroup of the persistent grid of min(units, ctas); with
+  // H, W <= 64 only the units spanning two heads or partial use one, so
+  // min(B*heads, workgroups) slots.
   const int64_t units = (BH * ((static_cast<int64_t>(H) * W + 31) / 32) + kBlocks12 - 1) / kBlocks12;
-  const int64_t slots = units < ctas ? units : ctas;
+  int64_t slots = units < ctas ? units : ctas;
+  if (attn_fused12_lds_bias(H, W) && BH < slots) slots = BH;
   return static_cast<size_t>(slots) * kBlocks12 * 32 * (H + W) * 4;
 }
 

@@ -361,9 +361,11 @@ def test_fused_workspace_bytes(lib):
     # 12-wave fused kernel (bf16, W % 32 == 0, H % 4 == 0, N >= 2048); a slot
     # is 6 blocks x 32 queries x (H + W) floats.  H, W <= 64: units inside one
     # head keep their bias rows in LDS, the others (spanning two heads, or a
-    # partial last unit) use one slot per b*heads, whatever the CU count.
+    # partial last unit) use one slot per b*heads, or per workgroup of the
+    # persistent grid of min(units, CUs) when that is fewer.
     assert _fused_ws(lib, 1, 12, 64, 64, BF16) == 12 * 192 * 128 * 4          # 1.2 MB
-    assert _fused_ws(lib, 1, 12, 64, 64, BF16, cus=8) == 12 * 192 * 128 * 4
+    assert _fused_ws(lib, 1, 12, 64, 64, BF16, cus=8) == 8 * 192 * 128 * 4
+    assert _fused_ws(lib, 32, 12, 64, 64, BF16) == 256 * 192 * 128 * 4       # 384 heads, 256 CUs
     assert _fused_ws(lib, 1, 1, 64, 64, BF16) == 192 * 128 * 4
     assert _fused_ws(lib, 2, 3, 48, 64, BF16) == 6 * 192 * 112 * 4
     assert _fused_ws(lib, 1, 2, 64, 32, BF16) == 2 * 192 * 96 * 4

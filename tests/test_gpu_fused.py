@@ -45,10 +45,11 @@ def _ws_bytes(H, W, BH=2, dtype="bf16"):
     if _small_grid(H, W):
         return 0
     if dtype == "bf16" and W % 32 == 0 and H % 4 == 0 and H * W >= 2048:
-        if H <= 64 and W <= 64:  # slots only for units spanning two heads or partial: one per b*heads
-            return BH * 6 * 32 * (H + W) * 4
         units = (BH * ((H * W + 31) // 32) + 5) // 6
-        return min(units, _cus()) * 6 * 32 * (H + W) * 4
+        slots = min(units, _cus())
+        if H <= 64 and W <= 64:  # slots only for units spanning two heads or partial: one per b*heads
+            slots = min(slots, BH)
+        return slots * 6 * 32 * (H + W) * 4
     rows = (H + 3) // 4 * 4 + (W + 15) // 16 * 16
     return _cus() * (2 * (256 * 64 + 2 * 256) + 256 * rows) * 4
 
@@ -112,6 +113,22 @@ def test_twelve_wave_fused_lds_bias(kw):
     _check(f"LDS bias {kw}", np.abs(G.f64(out) - ref))
     two, _, _ = G.gpu_run(d, config=6)  # the same 12-wave kernel in the two-call path
     assert torch.equal(out, two), "fused call differs from relpos_build + relpos_attn_fwd"
+
+
+def test_twelve_wave_fused_lds_bias_more_heads_than_workgroups():
+    """300 heads of 32x64: more b*heads than workgroups, so the units spanning
+    two heads use per-workgroup slots; bitwise against the two-call path on
+    the same kernel, and every output of three heads against the oracle."""
+    d = G.make("tiny", B=25, heads=12, H=32, W=64)
+    BH = 300
+    assert rp.fused_workspace_bytes(25, 12, 32, 64, torch.bfloat16, _cus()) == _ws_bytes(32, 64, BH=BH)
+    out = _fused(d)
+    two, _, _ = G.gpu_run(d, config=6)
+    assert torch.equal(out, two), "fused call differs from relpos_build + relpos_attn_fwd"
+    for b, h in ((0, 0), (12, 5), (24, 11)):  # first, a middle and the last head
+        sub = {**d, **{n: d[n][b:b + 1, h:h + 1] for n in ("q", "k", "v")}}
+        ref, _, _ = G.oracle_full(sub)
+        _check(f"300 heads, head ({b}, {h})", np.abs(G.f64(out[b:b + 1, h:h + 1]) - ref))
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125])
