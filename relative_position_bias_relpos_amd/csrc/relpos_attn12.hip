@@ -74,34 +74,6 @@ __device__ __forceinline__ int k_off(int o, int c) { return o * 128 + 16 * (c ^ 
 // groups of a 32-lane pass cover the 64 banks once.
 __device__ __forceinline__ int v_off(int o, int c) { return o * 128 + 16 * (c ^ (4 * ((o >> 1) & 1))); }
 
-typedef uint32_t __attribute__((ext_vector_type(4))) sgpr4;
-
-// Raw buffer descriptor words (base, no stride, `bytes` records, raw-buffer
-// flags) for the LDS-direct load below; wave-uniform.
-__device__ __forceinline__ sgpr4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32))) & 0xffffu;
-  return sgpr4{lo, hi, bytes, kBufFlags};
-}
-
-// One LDS-direct 16-byte buffer load per lane: lane L's 16 bytes at byte
-// offset voff + soff of the buffer land at LDS byte lds + 16*L (offsets past
-// the buffer's size read zeros).  Written as asm because the compiler, which
-// cannot tell LDS written this way from the LDS other instructions read,
-// otherwise waits for every outstanding vector load before each LDS read and
-// barrier that follows.  Nothing is returned in registers: the data is only
-// read after this wave's explicit vmcnt(0) wait and a workgroup barrier.
-__device__ __forceinline__ void lds_load16(sgpr4 rs, int voff, int soff, uint32_t lds) {
-  __asm__ volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
-      : "memory", "m0");
-}
-
 // Bias rows of one block of 32 queries (m0 .. m0+31 of grid row qh, W % 32 ==
 // 0) for the fused call, computed by one wave on 32x32x16 MFMA: axis 0 writes
 // rel_h [32][H] at dst, axis 1 rel_w [32][W] (the same products as

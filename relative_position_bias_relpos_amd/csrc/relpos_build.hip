@@ -51,6 +51,12 @@ namespace {
 constexpr int kD = 64;
 constexpr int kHStride = 72;   // floats per staged rel_h row (64 used)
 constexpr int kGStride = 104;  // floats per staged G row (95 used)
+// Table windows staged in LDS by build_kernel: 64 rows of T_h (8 KB) then 96
+// rows of T_w (12 KB), 128-byte rows whose 16-byte chunk c sits at chunk c ^
+// (row % 8).
+constexpr int kWinH = 0, kWinW = 8192, kWinBytes = 20480;
+static_assert(32 * kGStride * 4 <= kWinBytes, "the product staging must fit the window area");
+__device__ __forceinline__ int win_off(int r, int c) { return r * 128 + 16 * (c ^ (r & 7)); }
 
 // Cache policy of the row stores of build_kernel: sc1 (device scope: written
 // through to memory, so the kernel ends with no dirty L2 lines of rows to
@@ -88,10 +94,11 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ tw,
                                                    float* __restrict__ rel_h,
                                                    float* __restrict__ rel_w, int H, int W, int mtn) {
-  // One staging area for both products (the rel_h pass ends with a barrier
-  // before the rel_w pass writes): 13 KB, so that 12 one-wave workgroups fit
-  // a CU's LDS, as many as its registers allow.
-  __shared__ __attribute__((aligned(16))) float stage[32 * kGStride];
+  // 20 KB: the table windows the wave's MFMA operands come from (T_h rows at
+  // 0, T_w rows at 8 KB), then, once those operands are in registers, the
+  // staging area of both products (13 KB; the rel_h pass ends with a barrier
+  // before the rel_w pass writes).  8 one-wave workgroups per CU.
+  __shared__ __attribute__((aligned(16))) float stage[kWinBytes / 4];
   float* const stage_h = stage;
   float* const stage_g = stage;
   const int lane = threadIdx.x;
@@ -118,8 +125,6 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   // Every load is a raw buffer load whose out-of-range offsets read zeros:
   // no branch, so all of a chunk's loads are in flight together.
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row0 * kD, static_cast<uint32_t>(rows) * kD * 2);
-  const __amdgpu_buffer_rsrc_t rth = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
-  const __amdgpu_buffer_rsrc_t rtw = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
   const int dchunk = 16 * half;  // byte offset of this lane's 8 d values within a 16-wide slice
   // the unit's rel_h and rel_w rows (store targets)
   const __amdgpu_buffer_rsrc_t rsh =
@@ -132,29 +137,56 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml < rows ? ml * kD * 2 + 32 * kd + dchunk : kOob);
 
-  // B operands: table row per output column (rel_h) or per G column (rel_w)
+  // B operands: table row per output column (rel_h) or per G column (rel_w).
+  // Each chunk's rows form one contiguous window of the table, staged in LDS
+  // by LDS-direct loads of 1 KB (8 rows) each: the 64 lanes of a load touch 8
+  // cache lines, where loading the operands straight from the table touches
+  // 32 (one row per lane), which made the CU's vector-memory path the limit
+  // of the kernel's first microseconds (loads landed 3.6 us after the start
+  // at 64x64 with 12 heads).  Rows outside the table read zeros (negative
+  // offsets are out of range as unsigned offsets too).
+  const uint32_t lds0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) float*)stage))));
+  const sgpr4 wth = rsrc_words(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+  const sgpr4 wtw = rsrc_words(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+  // window of `rows8` pieces of 8 rows from table row t0 at LDS byte `at`
+  auto stage_window = [&](const sgpr4& rs, int t0, int rows8, int at) {
+    for (int p = 0; p < rows8; ++p) {
+      const int r = 8 * p + (lane >> 3);
+      lds_load16(rs, (t0 + r) * kD * 2 + 16 * ((lane & 7) ^ (r & 7)), 0, lds0 + at + 1024 * p);
+    }
+  };
+  // chunk n0 of rel_h: kh = n0 + j (j < 64) takes table row qh - kh + H - 1,
+  // window row 63 - j of the window from row qh + H - 1 - n0 - 63
+  auto window_h = [&](int n0) { stage_window(wth, qh + H - 1 - n0 - 63, 8, kWinH); };
+  // chunk n0 of rel_w: G column j (< 96) takes table row tlo + j
+  auto window_w = [&](int n0) { stage_window(wtw, m0 - n0 - 63 + W - 1, 12, kWinW); };
+  const unsigned char* const win = reinterpret_cast<const unsigned char*>(stage);
   u32x4 bh[2][4], bw[3][4];
-  auto load_h = [&](int n0) {
+  auto read_h = [&]() {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int kh = n0 + 32 * nt + ml;
-      const int off = kh < H ? (qh - kh + H - 1) * kD * 2 + dchunk : kOob;
 #pragma unroll
-      for (int kd = 0; kd < 4; ++kd) bh[nt][kd] = buf_load16(rth, off, 32 * kd);
+      for (int kd = 0; kd < 4; ++kd)
+        bh[nt][kd] = *reinterpret_cast<const u32x4*>(win + kWinH + win_off(63 - 32 * nt - ml, 2 * kd + half));
     }
   };
-  auto load_w = [&](int n0) {
-    const int tlo = m0 - n0 - 63 + W - 1;
+  auto read_w = [&]() {
 #pragma unroll
     for (int gt = 0; gt < 3; ++gt) {
-      const int t = tlo + 32 * gt + ml;
-      const int off = t >= 0 && t <= 2 * W - 2 ? t * kD * 2 + dchunk : kOob;
 #pragma unroll
-      for (int kd = 0; kd < 4; ++kd) bw[gt][kd] = buf_load16(rtw, off, 32 * kd);
+      for (int kd = 0; kd < 4; ++kd)
+        bw[gt][kd] = *reinterpret_cast<const u32x4*>(win + kWinW + win_off(32 * gt + ml, 2 * kd + half));
     }
   };
-  load_h(0);
-  load_w(0);
+  // before the windows are staged again over the product staging: this
+  // wave's reads of it are complete
+  auto lds_idle = [&]() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  window_h(0);
+  window_w(0);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_h();
+  read_w();
 
   // MFMA output register r of this lane: row 8*(r/4) + 4*half + r%4, column ml.
   auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
@@ -172,11 +204,16 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage_h[out_row(r) * kHStride + 32 * nt + ml] = acc[r];
     }
-    if (n0 + 64 < H) load_h(n0 + 64);
     __syncthreads();
     f32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4*>(stage_h + (sr + 4 * i) * kHStride + sc);
+    if (n0 + 64 < H) {
+      lds_idle();
+      window_h(n0 + 64);
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      read_h();
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = sr + 4 * i;
@@ -195,7 +232,6 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage_g[out_row(r) * kGStride + 32 * gt + ml] = g[r];
     }
-    if (n0 + 64 < W) load_w(n0 + 64);
     __syncthreads();
     // columns n0 + sc + e of row m take G[m, m - sc - e + 63]
     f32x4 v[8];
@@ -204,6 +240,12 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       const int m = sr + 4 * i;
       const float* gp = stage_g + m * kGStride + m - sc + 63;
       v[i] = f32x4{gp[0], gp[-1], gp[-2], gp[-3]};
+    }
+    if (n0 + 64 < W) {
+      lds_idle();
+      window_w(n0 + 64);
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      read_w();
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
