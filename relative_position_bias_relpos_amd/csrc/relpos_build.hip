@@ -267,8 +267,13 @@ __global__ __launch_bounds__(64) void build_small_kernel(const uint16_t* __restr
                                                          float* __restrict__ rel_h,
                                                          float* __restrict__ rel_w, int H, int W, int upb,
                                                          uint32_t mh, uint32_t mw) {
-  __shared__ __attribute__((aligned(16))) float gh[32 * kHStride];
-  __shared__ __attribute__((aligned(16))) float gw[32 * kHStride];
+  // The products gh, gw (32 rows of 72 floats each); before them, the two
+  // tables (rows of 128 bytes, chunk c of row r at chunk c ^ (r % 8); T_h at
+  // 0, T_w at 8 KB), staged by LDS-direct loads and read into registers.
+  __shared__ __attribute__((aligned(16))) float gsm[2 * 32 * kHStride];
+  static_assert(2 * 32 * kHStride * 4 >= 16384, "both tables must fit the product area");
+  float* const gh = gsm;
+  float* const gw = gsm + 32 * kHStride;
   const int lane = threadIdx.x;
   const int ml = lane & 31, half = lane >> 5;
   // units in (b*heads, 32-query block) order, XCD-matched like the kernel above
@@ -280,21 +285,38 @@ __global__ __launch_bounds__(64) void build_small_kernel(const uint16_t* __restr
   const size_t row0 = static_cast<size_t>(bhi) * N + i0;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row0 * kD, static_cast<uint32_t>(rows) * kD * 2);
-  const __amdgpu_buffer_rsrc_t rth = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
-  const __amdgpu_buffer_rsrc_t rtw = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
   const int dchunk = 16 * half;
   u32x4 a[4], bh[2][4], bw[2][4];
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml < rows ? ml * kD * 2 + 32 * kd + dchunk : kOob);
+  // B operands: table row j = 32*nt + ml (both tables have at most 63 rows,
+  // zeros past the last).  The tables go to LDS by LDS-direct loads of 8 rows
+  // each (8 cache lines per load, against 32 when each lane loads its own
+  // row), as in the kernel above; rows past the staged pieces hold whatever
+  // LDS held, and only feed product columns past 2L - 2, which are not read.
+  {
+    const uint32_t lds0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+        reinterpret_cast<size_t>((__attribute__((address_space(3))) float*)gsm))));
+    const sgpr4 wth = rsrc_words(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+    const sgpr4 wtw = rsrc_words(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+    const int ph = (2 * H - 1 + 7) / 8, pw = (2 * W - 1 + 7) / 8;
+    for (int p = 0; p < 8; ++p) {
+      const int r = 8 * p + (lane >> 3);
+      const int off = r * kD * 2 + 16 * ((lane & 7) ^ (r & 7));
+      if (p < ph) lds_load16(wth, off, 0, lds0 + 1024 * p);
+      if (p < pw) lds_load16(wtw, off, 0, lds0 + 8192 + 1024 * p);
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const unsigned char* const tb = reinterpret_cast<const unsigned char*>(gsm);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int j = 32 * nt + ml;  // table row
-    const int oh = j < 2 * H - 1 ? j * kD * 2 + dchunk : kOob;
-    const int ow = j < 2 * W - 1 ? j * kD * 2 + dchunk : kOob;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int j = 32 * nt + ml;  // table row
 #pragma unroll
-    for (int kd = 0; kd < 4; ++kd) {
-      bh[nt][kd] = buf_load16(rth, oh, 32 * kd);
-      bw[nt][kd] = buf_load16(rtw, ow, 32 * kd);
+      for (int kd = 0; kd < 4; ++kd) {
+        const int off = j * 128 + 16 * ((2 * kd + half) ^ (j & 7));
+        bh[nt][kd] = *reinterpret_cast<const u32x4*>(tb + off);
+        bw[nt][kd] = *reinterpret_cast<const u32x4*>(tb + 8192 + off);
+      }
     }
   }
   auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
