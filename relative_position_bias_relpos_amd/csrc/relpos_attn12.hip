@@ -79,36 +79,43 @@ __device__ __forceinline__ int v_off(int o, int c) { return o * 128 + 16 * (c ^ 
 // rel_h [32][H] at dst, axis 1 rel_w [32][W] (the same products as
 // relpos_build: rel_h against the reversed window of T_h, rel_w through the
 // 96 columns of q . T_w its 64-column chunks reach, read back along the
-// diagonal).  `stage` is this wave's LDS staging area (32 x 104 floats).
+// diagonal).  `a` holds the block's Q fragments.  `stage` is this wave's LDS
+// area (32 x 104 floats, LDS byte address stage_lds); each chunk's table
+// window (64 rows of T_h or 96 of T_w, contiguous in the table) is first
+// staged there by LDS-direct loads of 8 rows each (8 cache lines per load,
+// against 32 when each lane loads its own row), rows of 128 bytes with chunk
+// c at c ^ (row % 8), and the operands are read from it before the products
+// are staged over it.  Rows outside the table read zeros.
 template <bool BF16>
-__device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qrows,
-                                                const uint16_t* __restrict__ th,
+__device__ __forceinline__ void fused_bias_rows(const u32x4 (&a)[4], const uint16_t* __restrict__ th,
                                                 const uint16_t* __restrict__ tw, float* __restrict__ dst,
                                                 int axis, int qh, int m0, int H, int W, float* stage,
-                                                int lane) {
+                                                uint32_t stage_lds, int lane) {
   constexpr int kHS = 72, kGS = 104;  // staging row strides (floats)
   const int ml = lane & 31, half = lane >> 5;
-  const int dchunk = 16 * half;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qrows, 32 * kD * 2);
-  u32x4 a[4];
-#pragma unroll
-  for (int kd = 0; kd < 4; ++kd) a[kd] = buf_load16(rq, ml * kD * 2 + 32 * kd + dchunk);
   auto out_row = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
   const int sc = 4 * (lane & 15), sr = lane >> 4;
+  const unsigned char* const win = reinterpret_cast<const unsigned char*>(stage);
+  auto window = [&](const sgpr4& rs, int t0, int pieces) {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's reads of the area are done
+    for (int p = 0; p < pieces; ++p) {
+      const int r = 8 * p + (lane >> 3);
+      lds_load16(rs, (t0 + r) * kD * 2 + 16 * ((lane & 7) ^ (r & 7)), 0, stage_lds + 1024 * p);
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto wread = [&](int r, int c) { return *reinterpret_cast<const u32x4*>(win + r * 128 + 16 * (c ^ (r & 7))); };
   if (axis == 0) {
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
+    const sgpr4 rt = rsrc_words(th, static_cast<uint32_t>(2 * H - 1) * kD * 2);
     for (int n0 = 0; n0 < H; n0 += 64) {
-      // every table fragment of the chunk in flight at once (raw buffer loads,
-      // zeros past the table), then the MFMAs
+      // kh = n0 + j takes table row qh - kh + H - 1: window row 63 - j
+      window(rt, qh + H - 1 - n0 - 63, 8);
       u32x4 b[2][4];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int kh = n0 + 32 * nt + ml;
-        const int off = kh < H ? (qh - kh + H - 1) * kD * 2 + dchunk : kOob;
 #pragma unroll
-        for (int kd = 0; kd < 4; ++kd) b[nt][kd] = buf_load16(rt, off, 32 * kd);
+        for (int kd = 0; kd < 4; ++kd) b[nt][kd] = wread(63 - 32 * nt - ml, 2 * kd + half);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x16 acc{};
@@ -126,23 +133,18 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
         const f32x4 x = *reinterpret_cast<const f32x4*>(stage + m * kHS + sc);
         if (n < H) *reinterpret_cast<f32x4*>(dst + m * H + n) = x;  // H % 4 == 0 here
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   } else {
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
+    const sgpr4 rt = rsrc_words(tw, static_cast<uint32_t>(2 * W - 1) * kD * 2);
     for (int n0 = 0; n0 < W; n0 += 64) {
-      const int tlo = m0 - n0 - 63 + W - 1;
+      // G column j takes table row tlo + j: window row j
+      window(rt, m0 - n0 - 63 + W - 1, 12);
       u32x4 b[3][4];
 #pragma unroll
       for (int gt = 0; gt < 3; ++gt) {
-        const int t = tlo + 32 * gt + ml;
-        const int off = t >= 0 && t <= 2 * W - 2 ? t * kD * 2 + dchunk : kOob;
 #pragma unroll
-        for (int kd = 0; kd < 4; ++kd) b[gt][kd] = buf_load16(rt, off, 32 * kd);
+        for (int kd = 0; kd < 4; ++kd) b[gt][kd] = wread(32 * gt + ml, 2 * kd + half);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int gt = 0; gt < 3; ++gt) {
         f32x16 g{};
@@ -161,12 +163,10 @@ __device__ __forceinline__ void fused_bias_rows(const uint16_t* __restrict__ qro
         const f32x4 x{gp[0], gp[-1], gp[-2], gp[-3]};
         if (n < W) *reinterpret_cast<f32x4*>(dst + 32 * H + m * W + n) = x;  // W % 32 == 0 here
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
+static_assert(12 * 1024 <= 32 * 104 * 4, "a T_w window must fit a wave's staging area");
 
 // Bias rows kept in LDS (the fused call, single-head units, H <= 64 and W <=
 // 64, bf16 P): a workgroup spanning one head uses one 32 KB pair of each
@@ -398,11 +398,30 @@ __device__ __forceinline__ void attn12_unit(
     rh_rows = s2_rows;
     rw_rows = s2_rows + 32 * H;
   }
+  // ---- Q^T operand fragments of this wave's 32 queries -----------------------
+  const int ql = lane & 31;
+  const int qi = q0 + ql;
+  const bool qok = qi < N;
+  u32x4 qf[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd) {
+    qf[kd] = (qok && zero_q == 0) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
+                                  : u32x4{0, 0, 0, 0};
+  }
+
   if constexpr (FUSED && !LB && !S2) {
     float* brow = ws + (static_cast<size_t>(blockIdx.x) * kBlocks12 + blk) * 32 * (H + W);
     if (bvalid) {
-      fused_bias_rows<BF16>(q + (head + q0) * kD, th, tw, brow, par, q0 / W, q0 % W, H, W,
-                            reinterpret_cast<float*>(smem) + wave * 32 * 104, lane);
+      // the block's Q fragments (reloaded when scale == 0 zeroed them)
+      u32x4 qa[4];
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) {
+        qa[kd] = zero_q == 0 ? qf[kd] : *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half);
+      }
+      const uint32_t stage_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) unsigned char*)smem)))) + wave * 32 * 104 * 4;
+      fused_bias_rows<BF16>(qa, th, tw, brow, par, q0 / W, q0 % W, H, W,
+                            reinterpret_cast<float*>(smem) + wave * 32 * 104, stage_lds, lane);
     }
     // the rows are read back by this wave only (through the same L1)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -415,17 +434,6 @@ __device__ __forceinline__ void attn12_unit(
   const int band_tiles = (H + kTileRows - 1) / kTileRows;
   const int T = band_tiles * ((W + kTileCols - 1) / kTileCols);
   const int steps = (T + 1) / 2;
-
-  // ---- Q^T operand fragments of this wave's 32 queries -----------------------
-  const int ql = lane & 31;
-  const int qi = q0 + ql;
-  const bool qok = qi < N;
-  u32x4 qf[4];
-#pragma unroll
-  for (int kd = 0; kd < 4; ++kd) {
-    qf[kd] = (qok && zero_q == 0) ? *reinterpret_cast<const u32x4*>(q + (head + qi) * kD + 16 * kd + 8 * half)
-                                  : u32x4{0, 0, 0, 0};
-  }
 
   // ---- staging ------------------------------------------------------------------
   // Every load is an LDS-direct 16-byte buffer load: waves 0..7 bring in V
