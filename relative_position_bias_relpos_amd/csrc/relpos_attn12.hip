@@ -16,8 +16,9 @@
 //     output columns.  No workspace.
 //   * Per step the workgroup stages one tile pair (the next even and odd tile)
 //     per head it spans, all by LDS-direct 16-byte buffer loads that pass no
-//     data through registers: 8 waves load V, 4 load K, at the top of step t
-//     into the slot step t+1 reads (two LDS slots).  P.V runs on bf16 MFMA
+//     data through registers, at the top of step t into the slot step t+1
+//     reads (two LDS slots): waves 8..11 load K and V (waves 0..7 load V only
+//     where it is converted).  P.V runs on bf16 MFMA
 //     with P rounded to bf16 for bf16 inputs on grids of >= 2048 keys, so V is
 //     staged as loaded; fp16 inputs likewise in fp16.  Otherwise (bf16, fewer
 //     keys) P is fp16, and bf16 V lands in a raw area first and each V wave
@@ -436,9 +437,10 @@ __device__ __forceinline__ void attn12_unit(
   const int steps = (T + 1) / 2;
 
   // ---- staging ------------------------------------------------------------------
-  // Every load is an LDS-direct 16-byte buffer load: waves 0..7 bring in V
-  // (2 of a pair's 16 1-KB row blocks each, per head spanned), waves 8..11 K
-  // (4 row blocks each).
+  // Every load is an LDS-direct 16-byte buffer load: waves 8..11 bring in K
+  // and V (4 of each tile's 1-KB row blocks each, per head spanned), except
+  // that V to be converted (bf16 inputs with fp16 P) comes in on waves 0..7
+  // (2 row blocks each).
   const bool v_wave = wave < 8;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * kD * 2;
   const sgpr4 krs0 = rsrc_words(k + static_cast<size_t>(bhA) * N * kD, head_bytes);
@@ -446,7 +448,7 @@ __device__ __forceinline__ void attn12_unit(
   const sgpr4 vrs0 = rsrc_words(v + static_cast<size_t>(bhA) * N * kD, head_bytes);
   const sgpr4 vrs1 = rsrc_words(v + static_cast<size_t>(bhA + 1) * N * kD, head_bytes);
 
-  // V: wave w < 8 loads row blocks rb = 2*(w&3) + j (j = 0, 1) of tile w>>2
+  // V to convert: wave w < 8 loads row blocks rb = 2*(w&3) + j (j = 0, 1) of tile w>>2
   // of a pair into the raw area (lane L: row 8*rb + L/8, chunk L%8, as in
   // memory), and at the end of the step converts exactly those 16 bytes per
   // lane (bf16 -> fp16) into the slot's swizzled V tile.  No barrier is
@@ -534,6 +536,40 @@ __device__ __forceinline__ void attn12_unit(
         soff = 0;
       }
       lds_load16(rs, voff, soff, dst + i * 1024);
+    }
+  };
+  // V row blocks without conversion (bf16 P, or fp16 inputs): loaded by the
+  // K waves too, each its K blocks' (tile, rb), so that waves 0..7 issue no
+  // staging load.  Waves 8..11 are the third wave of their SIMDs, the last
+  // in the issue order, and have the slack: at 64x64 with 12 heads 63.3-63.4
+  // against 65.0-65.4 us with V on waves 0..7, 48x80 111.4 against 115.8-119.3
+  // us (spreading the loads over all 12 waves instead was slower: 119 us at
+  // 48x80).
+  auto v_dma_k = [&](const sgpr4& rs, TilePos pe, int pair_off) {
+    const TilePos p = k_tile == 0 ? pe : next_tile(pe, H);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = 8 * (4 * (kwv & 1) + i) + (lane >> 3);
+      const int goff = ((o >> 4) * W + (o & 15)) * (kD * 2) + 16 * ((lane & 7) ^ (4 * ((o >> 1) & 1)));
+      int voff, soff;
+      if constexpr (ALIGNED) {
+        voff = goff;
+        soff = p.kw < W ? tile_org(p) : 0;
+      } else {
+        const bool ok = p.kh + (o >> 4) < H && p.kw + (o & 15) < W;
+        voff = ok ? tile_org(p) + goff : kOob;
+        soff = 0;
+      }
+      lds_load16(rs, voff, soff, lds0 + pair_off + (2 + k_tile) * kTileBytes12 + (4 * (kwv & 1) + i) * 1024);
+    }
+  };
+  // The loads of one pair (per head spanned) into the pair area at pair_off.
+  auto stage_pair = [&](int e, const sgpr4& krs, const sgpr4& vrs, TilePos pe, int pair_off) {
+    if (v_wave) {
+      if constexpr (kConvertV) v_dma(e, vrs, pe, pair_off);
+    } else {
+      k_dma(krs, pe, pair_off);
+      if constexpr (!kConvertV) v_dma_k(vrs, pe, pair_off);
     }
   };
   auto slot_ptr = [&](int s) { return smem + s * kSlotBytes12; };
@@ -663,13 +699,8 @@ __device__ __forceinline__ void attn12_unit(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   const TilePos p0{0, 0};
-  if (v_wave) {
-    v_dma(0, vrs0, p0, 0);
-    if (two) v_dma(1, vrs1, p0, kPairBytes12);
-  } else {
-    k_dma(krs0, p0, 0);
-    if (two) k_dma(krs1, p0, kPairBytes12);
-  }
+  stage_pair(0, krs0, vrs0, p0, 0);
+  if (two) stage_pair(1, krs1, vrs1, p0, kPairBytes12);
   if constexpr (LB) stage_tables();  // beside pair 0's loads
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (v_wave) {
@@ -873,13 +904,8 @@ __device__ __forceinline__ void attn12_unit(
     // The loads of pair t+1 (issued right away: their latency is hidden by
     // this step's compute).
     auto stage = [&]() {
-      if (v_wave) {
-        v_dma(0, vrs0, pk, (cs ^ 1) * kSlotBytes12);
-        if (two) v_dma(1, vrs1, pk, (cs ^ 1) * kSlotBytes12 + kPairBytes12);
-      } else {
-        k_dma(krs0, pk, (cs ^ 1) * kSlotBytes12);
-        if (two) k_dma(krs1, pk, (cs ^ 1) * kSlotBytes12 + kPairBytes12);
-      }
+      stage_pair(0, krs0, vrs0, pk, (cs ^ 1) * kSlotBytes12);
+      if (two) stage_pair(1, krs1, vrs1, pk, (cs ^ 1) * kSlotBytes12 + kPairBytes12);
     };
     stage();
     compute(slot_ptr(cs), [&]() {
