@@ -17,18 +17,24 @@
 //   * Per step the workgroup stages one tile pair (the next even and odd tile)
 //     per head it spans, all by LDS-direct 16-byte buffer loads that pass no
 //     data through registers, at the top of step t into the slot step t+1
-//     reads (two LDS slots): waves 8..11 load K and V (waves 0..7 load V only
-//     where it is converted).  P.V runs on bf16 MFMA
-//     with P rounded to bf16 for bf16 inputs on grids of >= 2048 keys, so V is
-//     staged as loaded; fp16 inputs likewise in fp16.  Otherwise (bf16, fewer
-//     keys) P is fp16, and bf16 V lands in a raw area first and each V wave
-//     converts its own 16 bytes per lane to fp16 at the end of the step.
-//     Tiles are unpadded (8 KB) with XOR-swizzled 16-byte chunks so the MFMA
-//     operand reads hit every LDS bank once.
+//     reads (two LDS slots).  Waves 8..11, the third wave of each SIMD, load
+//     K and V; waves 0..7 load V only where it is converted, and run the key
+//     loop at wave priority 1.  P.V runs on bf16 MFMA with P rounded to bf16
+//     for bf16 inputs on grids of >= 2048 keys, so V is staged as loaded;
+//     fp16 inputs likewise in fp16.  Otherwise (bf16, fewer keys) P is fp16,
+//     and bf16 V lands in a raw area first and each of waves 0..7 converts
+//     its own 16 bytes per lane to fp16 at the end of the step.  Tiles are
+//     unpadded (8 KB) with XOR-swizzled 16-byte chunks so the MFMA operand
+//     reads hit every LDS bank once.
 //   * Inside a wave a step is plain: S^T = K Q^T (32x32x16 MFMA, rel_w in the
 //     accumulator's initial value), exp2 softmax with a lazy reference maximum,
 //     O^T += V^T P^T.  The three waves of a SIMD overlap one another's MFMA
 //     and VALU work.
+//   * The fused call (relpos_attn_fused) runs the same unit on a persistent
+//     grid, each unit first forming its blocks' bias rows on MFMA: into LDS
+//     for units inside one head on grids with H, W <= 64, else into a
+//     workspace slot (fused_bias_lds_phase1/2, fused_bias_slot_phase2,
+//     fused_bias_rows below).
 //
 // Lane layouts (S, P, the V transpose read) are the 32-query kernel's; only
 // the LDS addressing differs (swizzle instead of padding).
