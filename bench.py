@@ -316,7 +316,7 @@ def main():
         del src, dst
 
     # C calls with their arguments marshalled once, for the per-call loops
-    # (the Python binding's own cost, about 11 us a call, would otherwise bound
+    # (the Python binding's own cost, about 8-11 us a call, would otherwise bound
     # the shorter calls); they run the same C entry points as the binding.
     lib = rp._load()
     stream = rp._stream(q)
